@@ -1,0 +1,439 @@
+"""Pins for the CPU oracle: the pages' worked examples, closed forms,
+invariants, library cross-checks and exact brute force on tiny inputs.
+
+Nothing here needs a GPU. Each test names the passage it follows.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from conftest import golden
+import fp32_exact as fx
+from workloads import random_tensor
+
+
+def nhwc(a2d):
+    """A 2D single-channel image as an NHWC array [1,H,W,1]."""
+    a = np.asarray(a2d, dtype=np.float32)
+    return a.reshape(1, a.shape[0], a.shape[1], 1)
+
+
+def kkio(k2d):
+    k = np.asarray(k2d, dtype=np.float32)
+    return k.reshape(k.shape[0], k.shape[1], 1, 1)
+
+
+# --- worked examples -----------------------------------------------------------
+
+def test_lecture_arange_example(oracle_mod):
+    """CMU DLSys Lecture 14, section 4: arange(36) image, arange(9) filter."""
+    g = golden("lecture14_arange_patches.json")
+    A = np.arange(36, dtype=np.float32).reshape(6, 6)
+    Fk = np.arange(9, dtype=np.float32).reshape(3, 3)
+    Y = oracle_mod.conv2d_nhwc(nhwc(A), kkio(Fk))
+    assert Y.shape == (1, 4, 4, 1)
+    np.testing.assert_array_equal(Y[0, :, :, 0], np.array(g["output"], dtype=np.float64))
+    # Closed form derived from the index contract: Y[y,x] = Y[0,0] + 36x + 216y,
+    # since sum_{i,j}(3i+j) = 36 and the row stride of A is 6.
+    yy, xx = np.meshgrid(np.arange(4), np.arange(4), indexing="ij")
+    np.testing.assert_array_equal(Y[0, :, :, 0], 366 + 36 * xx + 216 * yy)
+    # The im2col route gives the same values.
+    np.testing.assert_array_equal(oracle_mod.conv2d_nhwc_im2col(nhwc(A), kkio(Fk)), Y)
+
+
+def test_lecture_patch_rows(oracle_mod):
+    """Lecture 14, sections 4-5: each patch is one row in (i,j,c) order."""
+    g = golden("lecture14_arange_patches.json")
+    A = np.arange(36, dtype=np.float32).reshape(6, 6)
+    cols = oracle_mod.im2col_nhwc(nhwc(A), 3, 3)
+    assert list(cols.shape) == g["patch_matrix_shape"]
+    np.testing.assert_array_equal(cols[0], g["patch_row_0"])
+    np.testing.assert_array_equal(cols[1], g["patch_row_1"])
+    assert cols.size == g["patch_values"] and A.size == g["input_values"]
+    # The overlapping patch view of section 4 (harness stride handling).
+    P = np.lib.stride_tricks.as_strided(A, shape=(4, 4, 3, 3), strides=A.strides + A.strides,
+                                        writeable=False)
+    assert list(P.strides) == g["patch_view_byte_strides"]
+    assert P[0, 0, 0, 1] == P[0, 1, 0, 0] == A[0, 1]
+    assert np.shares_memory(P, A) and not np.shares_memory(P.reshape(16, 9), A)
+    np.testing.assert_array_equal(P.reshape(16, 9), cols)
+
+
+def test_lecture_tile_view():
+    """Lecture 14, section 3: a view re-addresses, packing re-orders (the test
+    harness relies on numpy strides this way for non-contiguous inputs)."""
+    g = golden("lecture14_tile_view.json")
+    A = np.arange(36, dtype=np.float32).reshape(6, 6)
+    assert list(A.strides) == g["array"]["byte_strides"]
+    T = np.lib.stride_tricks.as_strided(A, shape=(3, 3, 2, 2), strides=(48, 8, 24, 4))
+    assert list(T.strides) == g["tile_view_byte_strides"]
+    np.testing.assert_array_equal(T[0, 0].ravel(), g["first_tile"])
+    np.testing.assert_array_equal(A.reshape(3, 3, 2, 2)[0, 0].ravel(), g["plain_reshape_first_tile"])
+    Tc = np.ascontiguousarray(T)
+    assert list(Tc.strides) == g["packed_byte_strides"]
+    np.testing.assert_array_equal(Tc.ravel()[:8], g["packed_sequence_start"])
+
+
+def test_lecture_storage_bill(oracle_mod):
+    """Lecture 14, section 6: patch matrix size and expansion ratio."""
+    g = golden("lecture14_storage_bill.json")
+    s = g["shape"]
+    X = np.zeros((s["N"], s["H"], s["W"], s["Cin"]), dtype=np.float32)
+    cols = oracle_mod.im2col_nhwc(X, s["K"], s["K"])
+    assert list(cols.shape) == g["patch_matrix_shape"]
+    v = g["values"]
+    assert X.size == v["input"] and cols.size == v["patch_matrix"]
+    assert s["K"] * s["K"] * s["Cin"] * s["Cout"] == v["filter"]
+    Ho = oracle_mod.out_size(s["H"], s["K"])
+    assert s["N"] * Ho * Ho * s["Cout"] == v["output"]
+    assert cols.size / X.size == g["rho"] == Ho * Ho * s["K"] ** 2 / (s["H"] * s["W"])
+    mb = g["megabytes_f32"]
+    assert X.nbytes / 1e6 == pytest.approx(mb["input"]) and cols.nbytes / 1e6 == pytest.approx(mb["patch_matrix"])
+    sm = g["small_example"]
+    assert sm["patch_values"] / sm["input_values"] == sm["ratio"]
+
+
+def test_wxb_window_with_bias(oracle_mod):
+    """'Convolution Is Wx+b', sections 'One window...' / 'The matrix connection'."""
+    g = golden("wxb_1d_examples.json")["window"]
+    x = np.asarray(g["x"], np.float32).reshape(1, 1, -1, 1)
+    k = np.asarray(g["k"], np.float32).reshape(1, -1, 1, 1)
+    b = np.asarray([g["bias"]], np.float32)
+    Y = oracle_mod.conv2d_nhwc(x, k, bias=b)
+    np.testing.assert_array_equal(Y.ravel(), g["y"])
+    # The same window sum through the depthwise loop (one channel), both modes.
+    for mode in ("exact", "fast"):
+        Yd = oracle_mod.depthwise_nchw(np.asarray(g["x"], np.float32).reshape(1, 1, 1, -1),
+                                       np.asarray(g["k"], np.float32).reshape(1, 1, -1), bias=b, mode=mode)
+        np.testing.assert_array_equal(Yd.ravel(), g["y"])
+
+
+@pytest.mark.parametrize("case", ["average", "difference", "motif"])
+def test_wxb_three_1d_uses(oracle_mod, case):
+    """'Convolution Is Wx+b', section 'Three ways to use the same 1D operation'."""
+    g = golden("wxb_1d_examples.json")[case]
+    k = [1 / 3] * 3 if case == "average" else g["k"]
+    x = np.asarray(g["x"], np.float32).reshape(1, 1, -1, 1)
+    Y = oracle_mod.conv2d_nhwc(x, np.asarray(k, np.float32).reshape(1, -1, 1, 1))
+    tol = 1e-6 if case == "average" else 0
+    np.testing.assert_allclose(Y.ravel(), g["y"], rtol=0, atol=tol)
+
+
+def test_wxb_two_filter_gemm(oracle_mod):
+    """'Convolution Is Wx+b', section 'The matrix connection': two filters."""
+    g = golden("wxb_1d_examples.json")["two_filters"]
+    x = np.asarray(g["x"], np.float32).reshape(1, 1, -1, 1)
+    K = np.asarray(g["K_taps_by_filters"], np.float32).reshape(1, 3, 1, 2)
+    Y = oracle_mod.conv2d_nhwc(x, K, bias=np.asarray(g["bias"], np.float32))
+    np.testing.assert_array_equal(Y[0, 0], g["y_positions_by_filters"])
+
+
+def test_wxb_small_2d(oracle_mod):
+    """'Convolution Is Wx+b', section 'Why 1D? Why 2D?': 3x3 image, 2x2 filter."""
+    g = golden("wxb_2d_examples.json")["small"]
+    Y = oracle_mod.conv2d_nhwc(nhwc(g["image"]), kkio(g["filter"]))
+    np.testing.assert_array_equal(Y[0, :, :, 0], g["output"])
+    Yd = oracle_mod.depthwise_nchw(np.asarray(g["image"], np.float32)[None, None],
+                                   np.asarray(g["filter"], np.float32)[None])
+    np.testing.assert_array_equal(Yd[0, 0], g["output"])
+
+
+def sobel_image():
+    img = np.zeros((6, 6), np.float32)
+    img[:, 3:] = 1
+    return img
+
+
+def test_wxb_sobel(oracle_mod):
+    """'Convolution Is Wx+b', section 'Build an image-gradient map': Gx and Gy as
+    two output channels of one dense conv (the [16,9] @ [9,2] view), and as a
+    depthwise conv with multiplier 2."""
+    g = golden("wxb_2d_examples.json")["sobel"]
+    img = sobel_image()
+    F = np.stack([np.asarray(g["gx"], np.float32), np.asarray(g["gy"], np.float32)], axis=-1)
+    Y = oracle_mod.conv2d_nhwc(nhwc(img), F.reshape(3, 3, 1, 2))
+    np.testing.assert_array_equal(Y[0, :, :, 0], g["gx_output"])
+    np.testing.assert_array_equal(Y[0, :, :, 1], g["gy_output"])
+    cols = oracle_mod.im2col_nhwc(nhwc(img), 3, 3)
+    np.testing.assert_array_equal(cols[1], g["patch_row_at_0_1"])     # output (row 0, col 1)
+    w = np.stack([np.asarray(g["gx"], np.float32), np.asarray(g["gy"], np.float32)])
+    for mode in ("exact", "fast"):
+        Yd = oracle_mod.depthwise_nchw(img[None, None], w, mode=mode)
+        np.testing.assert_array_equal(Yd[0, 0], g["gx_output"])
+        np.testing.assert_array_equal(Yd[0, 1], g["gy_output"])
+
+
+def test_out_size_rule(oracle_mod):
+    """'Convolution Is Wx+b', section 'Why 1D? Why 2D?': output-size rule."""
+    g = golden("wxb_1d_examples.json")["out_size"]
+    assert oracle_mod.out_size(g["in"], g["k"]) == g["out"]
+    # The depthwise workload shapes (stride s, pad K//2).
+    assert oracle_mod.out_size(56, 5, 2, 2, 1) == 28
+    assert oracle_mod.out_size(112, 3, 1, 1, 1) == 112
+    assert oracle_mod.out_size(112, 3, 2, 1, 1) == 56
+    assert oracle_mod.out_size(14, 5, 2, 2, 1) == 7
+    assert oracle_mod.out_size(7, 5, 1, 2, 1) == 7
+    assert oracle_mod.out_size(7, 3, 1, 0, 3) == 1      # effective kernel 7
+    assert oracle_mod.out_size(7, 3, 1, 0, 4) <= 0      # effective kernel 9 > 7
+
+
+# --- invariants ----------------------------------------------------------------
+
+SHAPES = [  # (N, H, W, Cin, K, Cout): small, non-square, distinct channels
+    (1, 5, 7, 3, 3, 2), (2, 6, 4, 5, 2, 3), (2, 4, 9, 1, 1, 4), (1, 3, 3, 2, 3, 3),
+    (3, 7, 5, 4, 4, 1), (1, 8, 6, 6, 1, 5),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+def test_k1_is_matmul_and_shifted_matmuls(oracle_mod, shape):
+    """Lecture 14, section 2: K=1 is X @ F[0,0]; for larger K the output is the
+    sum of K^2 shifted channel matmuls. Integer-valued inputs keep every sum
+    exact, so any accumulation order must give identical values."""
+    N, H, W, C, K, O = shape
+    seed = hash(shape) & 0xFFFF
+    X = random_tensor((N, H, W, C), seed, integer_range=4).numpy()
+    F = random_tensor((K, K, C, O), seed + 1, integer_range=4).numpy()
+    Y = oracle_mod.conv2d_nhwc(X, F)
+    Ho, Wo = H - K + 1, W - K + 1
+    ref = np.zeros((N, Ho, Wo, O))
+    for i in range(K):
+        for j in range(K):
+            ref += X[:, i:i + Ho, j:j + Wo, :].astype(np.float64) @ F[i, j].astype(np.float64)
+    np.testing.assert_array_equal(Y, ref)
+    np.testing.assert_array_equal(oracle_mod.conv2d_nhwc_im2col(X, F), Y)
+    X1 = X.astype(np.float64).reshape(-1, C) @ F[0, 0].astype(np.float64)
+    np.testing.assert_array_equal(oracle_mod.conv2d_nhwc(X, F[:1, :1]).reshape(-1, O), X1)
+
+
+@pytest.mark.parametrize("seed", [1, 2, 3])
+def test_full_image_filter(oracle_mod, seed):
+    """Lecture 14, section 5 test advice: a square input whose filter spans the
+    whole image gives one output per image, X[n].ravel() @ F.reshape(-1, O)."""
+    N, S, C, O = 2, 5, 3, 4
+    X = random_tensor((N, S, S, C), seed).numpy()
+    F = random_tensor((S, S, C, O), seed + 10).numpy()
+    Y = oracle_mod.conv2d_nhwc(X, F)
+    assert Y.shape == (N, 1, 1, O)
+    ref = X.reshape(N, -1).astype(np.float64) @ F.reshape(-1, O).astype(np.float64)
+    np.testing.assert_allclose(Y[:, 0, 0, :], ref, rtol=1e-13, atol=1e-13)
+
+
+GENERAL = [  # (N,H,W,Cin,KH,KW,Cout, stride, pad, dil, groups)
+    (2, 7, 9, 3, 3, 3, 4, 1, 0, 1, 1),
+    (1, 8, 6, 4, 3, 2, 6, 2, 1, 1, 2),
+    (2, 9, 9, 6, 3, 3, 6, 1, 2, 2, 3),
+    (1, 10, 7, 4, 5, 5, 4, (2, 1), (2, 1), 1, 4),
+    (1, 6, 5, 2, 1, 3, 3, 1, (0, 1), (1, 2), 1),
+]
+
+
+@pytest.mark.parametrize("case", GENERAL)
+def test_dense_matches_torch_conv2d(oracle_mod, case):
+    """Lecture 14, section 1: a library comparison converts NHWC inputs with
+    transpose(0,3,1,2) and KKIO filters with transpose(3,2,0,1). torch's CPU
+    conv2d in fp64 must agree with the loops, including the stride / padding /
+    dilation / groups superset."""
+    N, H, W, C, KH, KW, O, s, p, d, g = case
+    X = random_tensor((N, H, W, C), 7).numpy()
+    F = random_tensor((KH, KW, C // g, O), 8).numpy()
+    b = random_tensor((O,), 9).numpy()
+    Y = oracle_mod.conv2d_nhwc(X, F, bias=b, stride=s, padding=p, dilation=d, groups=g)
+    xt = torch.from_numpy(X).double().permute(0, 3, 1, 2)
+    ft = torch.from_numpy(F).double().permute(3, 2, 0, 1)
+    ref = torch.nn.functional.conv2d(xt, ft, torch.from_numpy(b).double(), stride=s, padding=p,
+                                     dilation=d, groups=g).permute(0, 2, 3, 1).numpy()
+    np.testing.assert_allclose(Y, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_dense_noncontiguous_input(oracle_mod):
+    """Lecture 14, section 5: the patch view uses the actual input strides, so
+    sliced or transposed inputs keep their logical meaning."""
+    base = random_tensor((2, 9, 11, 8), 21).numpy()
+    F = random_tensor((3, 3, 3, 5), 22).numpy()
+    views = [base[:, 1:8, 2:10, 1:4],                          # sliced, channel stride 1
+             base[:, ::2, ::2, ::2][..., :3],                  # stepped, channel stride 2
+             np.ascontiguousarray(base[..., :3].transpose(0, 2, 1, 3)).transpose(0, 2, 1, 3)]
+    for v in views:
+        assert not v.flags["C_CONTIGUOUS"]
+        np.testing.assert_array_equal(oracle_mod.conv2d_nhwc(v, F), oracle_mod.conv2d_nhwc(np.ascontiguousarray(v), F))
+
+
+def test_dense_translation_equivariance(oracle_mod):
+    """'Convolution Is Wx+b', section 'Why convolution is still important':
+    at stride 1, shifting the input by one pixel shifts the response by one,
+    away from the borders."""
+    X = random_tensor((1, 9, 10, 3), 31).numpy()
+    F = random_tensor((3, 3, 3, 2), 32).numpy()
+    Xs = np.zeros_like(X)
+    Xs[:, 1:, 1:, :] = X[:, :-1, :-1, :]
+    Y, Ys = oracle_mod.conv2d_nhwc(X, F), oracle_mod.conv2d_nhwc(Xs, F)
+    np.testing.assert_array_equal(Ys[:, 1:, 1:, :], Y[:, :-1, :-1, :])
+
+
+def test_dense_sampled_equals_full(oracle_mod):
+    X = random_tensor((2, 7, 6, 5), 41).numpy()
+    F = random_tensor((2, 3, 5, 3), 42).numpy()
+    Y = oracle_mod.conv2d_nhwc(X, F)
+    idx = np.array([0, 1, 17, 45, Y.size - 1], dtype=np.int64)
+    np.testing.assert_array_equal(oracle_mod.conv2d_nhwc_at(X, F, idx), Y.ravel()[idx])
+
+
+# --- depthwise -----------------------------------------------------------------
+
+def brute_depthwise(X, w, bias, stride, pad, dil, mode):
+    """Exact-rational brute force of the depthwise output definition
+    ("Depthwise convolution", section 'What each output is')."""
+    N, C, H, W = X.shape
+    Cout, KH, KW = w.shape
+    mult = Cout // C
+    sh, sw = stride
+    ph, pw = pad
+    dh, dw = dil
+    Ho = (H + 2 * ph - (dh * (KH - 1) + 1)) // sh + 1
+    Wo = (W + 2 * pw - (dw * (KW - 1) + 1)) // sw + 1
+    out = np.empty((N, Cout, Ho, Wo), np.float32)
+    for n in range(N):
+        for oc in range(Cout):
+            ic = oc // mult
+            for oy in range(Ho):
+                for ox in range(Wo):
+                    acc = 0.0
+                    for ky in range(KH):
+                        for kx in range(KW):
+                            r, c = oy * sh + ky * dh - ph, ox * sw + kx * dw - pw
+                            xv = float(X[n, ic, r, c]) if (0 <= r < H and 0 <= c < W) else 0.0
+                            wv = float(w[oc, ky, kx])
+                            if mode == "exact":
+                                acc = fx.add(acc, fx.mul(wv, xv))
+                            else:
+                                acc = fx.fma(wv, xv, acc)
+                    if bias is not None:
+                        acc = fx.add(acc, float(bias[oc]))
+                    if mode == "exact" and math.isnan(acc):
+                        acc = fx.from_bits(0x7FC00000)
+                    out[n, oc, oy, ox] = acc
+    return out
+
+
+DW_CASES = [  # (N,C,H,W, mult, KH,KW, stride, pad, dil, bias)
+    (1, 2, 5, 6, 1, 3, 3, (1, 1), (1, 1), (1, 1), False),
+    (2, 1, 7, 5, 2, 3, 2, (2, 1), (1, 0), (1, 1), True),
+    (1, 3, 6, 7, 1, 5, 5, (2, 2), (2, 2), (1, 1), False),
+    (1, 2, 8, 8, 3, 3, 3, (1, 2), (2, 2), (2, 2), True),
+    (1, 1, 9, 4, 1, 2, 3, (3, 3), (0, 1), (1, 1), False),
+]
+
+
+@pytest.mark.parametrize("case", DW_CASES)
+@pytest.mark.parametrize("mode", ["exact", "fast"])
+def test_depthwise_bitwise_brute_force(oracle_mod, case, mode):
+    """Depthwise oracle vs an exact-rational model of each fp32 step; bits must match."""
+    N, C, H, W, m, KH, KW, s, p, d, has_bias = case
+    seed = hash(case) & 0xFFFF
+    X = random_tensor((N, C, H, W), seed).numpy()
+    w = random_tensor((C * m, KH, KW), seed + 1).numpy()
+    b = random_tensor((C * m,), seed + 2).numpy() if has_bias else None
+    got = oracle_mod.depthwise_nchw(X, w, bias=b, stride=s, padding=p, dilation=d, mode=mode)
+    ref = brute_depthwise(X, w, b, s, p, d, mode)
+    np.testing.assert_array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+@pytest.mark.parametrize("mode", ["exact", "fast"])
+def test_depthwise_subnormal_bitwise(oracle_mod, mode):
+    """Products and sums in the subnormal range keep IEEE gradual underflow."""
+    X = (random_tensor((1, 2, 6, 6), 51).numpy() * np.float32(2.0 ** -70)).astype(np.float32)
+    w = (random_tensor((2, 3, 3), 52).numpy() * np.float32(2.0 ** -70)).astype(np.float32)
+    got = oracle_mod.depthwise_nchw(X, w, padding=1, mode=mode)
+    ref = brute_depthwise(X, w, None, (1, 1), (1, 1), (1, 1), mode)
+    assert np.any((got != 0) & (np.abs(got) < np.finfo(np.float32).tiny))    # subnormals occur
+    np.testing.assert_array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+def test_depthwise_exact_vs_fast_rounding(oracle_mod):
+    """Exact mode rounds the product before the sum; fast mode fuses them.
+    Taps (w, x): (-1, 1) then (1+2^-12, 1+2^-12). The second product is
+    1 + 2^-11 + 2^-24, a tie that rounds to 1 + 2^-11, so exact mode gives
+    2^-11 while the fused form keeps 2^-11 + 2^-24."""
+    a = np.float32(1 + 2.0 ** -12)
+    X = np.array([1, a], np.float32).reshape(1, 1, 1, 2)
+    w = np.array([-1, a], np.float32).reshape(1, 1, 2)
+    assert oracle_mod.depthwise_nchw(X, w, mode="exact").item() == 2.0 ** -11
+    assert oracle_mod.depthwise_nchw(X, w, mode="fast").item() == 2.0 ** -11 + 2.0 ** -24
+
+
+def bits(a):
+    return np.asarray(a, np.float32).view(np.uint32)
+
+
+def test_depthwise_special_values_exact(oracle_mod):
+    """'Depthwise convolution', section 'What each output is': padding is a real
+    zero (an infinite weight meeting it gives NaN), NaN results are rewritten to
+    0x7FC00000, and an accumulator that starts at +0 never ends at -0."""
+    nan_payload = fx.from_bits(0xFFC12345)           # negative NaN with a payload
+    X = np.array([[1.0, 2.0, 3.0], [4.0, nan_payload, 6.0], [7.0, 8.0, 9.0]], np.float32)[None, None]
+    w = np.ones((1, 3, 3), np.float32)
+    Y = oracle_mod.depthwise_nchw(X, w, padding=1, mode="exact")
+    assert np.all(bits(Y) == 0x7FC00000)                 # every window sees the centre NaN
+    # An infinite weight in a corner tap: only windows whose corner is padding get NaN.
+    X = np.ones((1, 1, 3, 3), np.float32)
+    w = np.zeros((1, 3, 3), np.float32)
+    w[0, 0, 0] = np.inf
+    Y = oracle_mod.depthwise_nchw(X, w, padding=1, mode="exact")
+    assert bits(Y)[0, 0, 0, 0] == 0x7FC00000                  # corner tap is padding: inf * 0
+    assert Y[0, 0, 1, 1] == np.inf                            # corner tap reads X = 1
+    # +inf + -inf cancels to NaN.
+    X = np.array([[1.0, 1.0]], np.float32)[None, None]
+    w = np.array([[[np.inf, -np.inf]]], np.float32)
+    assert bits(oracle_mod.depthwise_nchw(X, w, mode="exact")).item() == 0x7FC00000
+    # Negative weights times +0 inputs give -0 products; +0 + -0 = +0.
+    X = np.zeros((1, 1, 3, 3), np.float32)
+    w = -np.ones((1, 2, 2), np.float32)
+    Y = oracle_mod.depthwise_nchw(X, w, mode="exact")
+    assert np.all(bits(Y) == 0)
+    # Fast mode: NaN stays NaN (payload unspecified) and padding still multiplies.
+    Yf = oracle_mod.depthwise_nchw(np.ones((1, 1, 3, 3), np.float32),
+                                   np.where(np.arange(9).reshape(1, 3, 3) == 0, np.inf, 0).astype(np.float32),
+                                   padding=1, mode="fast")
+    assert np.isnan(Yf[0, 0, 0, 0]) and Yf[0, 0, 1, 1] == np.inf
+
+
+@pytest.mark.parametrize("case", DW_CASES)
+def test_depthwise_equals_block_diagonal_dense(oracle_mod, case):
+    """'Depthwise convolution': groups == C, output channel oc reads input
+    channel oc / mult. So depthwise equals the dense conv with the
+    block-diagonal filter F[i,j,c,o] = w[o,i,j] * [c == o // mult], and the
+    grouped dense conv with groups = C. Integer inputs keep every sum exact."""
+    N, C, H, W, m, KH, KW, s, p, d, has_bias = case
+    seed = (hash(case) & 0xFFFF) + 5
+    X = random_tensor((N, C, H, W), seed, integer_range=3).numpy()
+    w = random_tensor((C * m, KH, KW), seed + 1, integer_range=3).numpy()
+    b = random_tensor((C * m,), seed + 2, integer_range=3).numpy() if has_bias else None
+    Xn = np.ascontiguousarray(X.transpose(0, 2, 3, 1))
+    Fblock = np.zeros((KH, KW, C, C * m), np.float32)
+    for o in range(C * m):
+        Fblock[:, :, o // m, o] = w[o]
+    Fgroup = np.ascontiguousarray(w.transpose(1, 2, 0)[:, :, None, :])
+    for mode in ("exact", "fast"):
+        Yd = oracle_mod.depthwise_nchw(X, w, bias=b, stride=s, padding=p, dilation=d, mode=mode)
+        for F, g in ((Fblock, 1), (Fgroup, C)):
+            Yn = oracle_mod.conv2d_nhwc(Xn, F, bias=b, stride=s, padding=p, dilation=d, groups=g)
+            np.testing.assert_array_equal(Yd, Yn.transpose(0, 3, 1, 2).astype(np.float32))
+
+
+@pytest.mark.parametrize("case", DW_CASES)
+def test_depthwise_matches_torch(oracle_mod, case):
+    """torch's CPU conv2d with groups = C and weights viewed as [Cout,1,KH,KW]."""
+    N, C, H, W, m, KH, KW, s, p, d, has_bias = case
+    X = random_tensor((N, C, H, W), 61).numpy()
+    w = random_tensor((C * m, KH, KW), 62).numpy()
+    b = random_tensor((C * m,), 63).numpy() if has_bias else None
+    ref = torch.nn.functional.conv2d(torch.from_numpy(X).double(),
+                                     torch.from_numpy(w).double().view(C * m, 1, KH, KW),
+                                     None if b is None else torch.from_numpy(b).double(),
+                                     stride=s, padding=p, dilation=d, groups=C).numpy()
+    for mode in ("exact", "fast"):
+        got = oracle_mod.depthwise_nchw(X, w, bias=b, stride=s, padding=p, dilation=d, mode=mode)
+        np.testing.assert_allclose(got, ref, rtol=1e-5, atol=1e-5)
