@@ -1,0 +1,291 @@
+"""Throughput of the forward-convolution hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--mode cold|warm]
+                    [--no-cpu-baseline] [--no-secondary]
+
+A step is one launch of the dense 3x3 bf16 layer (X[32,58,58,64],
+F[3,3,64,64] -> Y[32,56,56,64], bf16 output, fp32 accumulation) through the C
+ABI. Inputs are resident in HBM before the timed region. In the default cold
+mode the steps rotate over enough distinct X/F/Y buffer sets (>= 1 GB) that
+each launch reads its operands from HBM rather than from the 256 MB
+memory-side cache; warm mode reuses one set.
+
+Launches are captured once into a HIP graph (torch.cuda.CUDAGraph) and
+replayed, so host launch overhead does not starve a kernel that runs for a
+few microseconds. The timed region is bracketed by synchronisations and HIP
+events on the stream the kernels are launched on.
+
+Prints ONE JSON line. Besides the headline it carries `secondary`: the other
+workloads (1x1 bf16 and fp32, the depthwise exact layer, the depthwise sweep)
+measured the same way, each against its own roofline.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+BF16_MFMA_PEAK_TFLOPS = 2516.6   # dense bf16 MFMA (256 CU x 4096 FLOP/clk x 2.4 GHz)
+F32_MFMA_PEAK_TFLOPS = 157.3     # dense fp32 MFMA
+COLD_BYTES = 1 << 30             # rotate at least this much distinct memory in cold mode
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--mode", choices=["cold", "warm"], default="cold")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--trials", type=int, default=3)
+    return ap.parse_args()
+
+
+class Runner:
+    """Holds S buffer sets for one workload and a graph of S launches."""
+
+    def __init__(self, name, make_set, launch, set_bytes, mode, max_sets=None):
+        import torch
+        self.torch = torch
+        self.name = name
+        want = 1 if mode == "warm" else max(1, math.ceil(COLD_BYTES / set_bytes))
+        if max_sets:
+            want = min(want, max_sets)
+        self.sets = [make_set(i) for i in range(want)]
+        self.launch = launch
+        self.graph = None
+
+    def capture(self, reps_per_graph):
+        torch = self.torch
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):          # warm the launch path outside capture
+            for st in self.sets:
+                self.launch(st)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            for _ in range(reps_per_graph):
+                for st in self.sets:
+                    self.launch(st)
+        torch.cuda.synchronize()
+        self.launches_per_replay = reps_per_graph * len(self.sets)
+
+    def time(self, steps, warmup, trials):
+        """Median ms per launch over `trials` timed regions of >= `steps` launches."""
+        torch = self.torch
+        replays = max(1, math.ceil(steps / self.launches_per_replay))
+        for _ in range(max(1, math.ceil(warmup / self.launches_per_replay))):
+            self.graph.replay()
+        torch.cuda.synchronize()
+        results = []
+        for _ in range(trials):
+            start = torch.cuda.Event(enable_timing=True)
+            end = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            start.record()
+            for _ in range(replays):
+                self.graph.replay()
+            end.record()
+            torch.cuda.synchronize()
+            results.append(start.elapsed_time(end) / (replays * self.launches_per_replay))
+        results.sort()
+        return results[len(results) // 2], replays * self.launches_per_replay
+
+
+def dense_runner(work, mode, out_dtype_name, dtype_name=None):
+    import torch
+    import convolution_forward_amd as cf
+    import workloads as wl
+
+    dt = dtype_name or work.dtype
+    X0, F0 = wl.dense_inputs(work, dtype=dt)
+    Ho, Wo = work.H - work.KH + 1, work.W - work.KW + 1
+    ydt = {"bf16": torch.bfloat16, "f32": torch.float32}[out_dtype_name]
+    lib = cf.load_library()
+    xdt = cf.CONV_BF16 if dt == "bf16" else cf.CONV_F32
+    ydc = cf.CONV_BF16 if out_dtype_name == "bf16" else cf.CONV_F32
+    esz = 2 if dt == "bf16" else 4
+    ysz = 2 if out_dtype_name == "bf16" else 4
+    set_bytes = X0.numel() * esz + F0.numel() * esz + work.N * Ho * Wo * work.Cout * ysz
+
+    def make_set(i):
+        X = X0.to("cuda") if i == 0 else X0.to("cuda").clone()
+        F = F0.to("cuda") if i == 0 else F0.to("cuda").clone()
+        Y = torch.empty((work.N, Ho, Wo, work.Cout), dtype=ydt, device="cuda")
+        return (X, F, Y)
+
+    def launch(st):
+        X, F, Y = st
+        rc = lib.conv2d_nhwc_fwd(X.data_ptr(), None, F.data_ptr(), None, Y.data_ptr(), None, work.N, work.H, work.W,
+                                 work.Cin, work.KH, work.KW, work.Cout, xdt, ydc,
+                                 torch.cuda.current_stream().cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"conv2d_nhwc_fwd failed: {cf.status_str(rc)}")
+
+    flops = 2.0 * work.N * Ho * Wo * work.Cout * work.KH * work.KW * work.Cin
+    return Runner(work.name, make_set, launch, set_bytes, mode), flops, set_bytes
+
+
+def dw_runner(work, mode, exact):
+    import torch
+    import convolution_forward_amd as cf
+    import workloads as wl
+
+    X0, w0 = wl.depthwise_inputs(work)
+    Ho = cf.out_size(work.H, work.KH, work.stride, work.pad, work.dil)
+    Wo = cf.out_size(work.W, work.KW, work.stride, work.pad, work.dil)
+    Cout = work.C * work.mult
+    lib = cf.load_library()
+    set_bytes = (X0.numel() + w0.numel() + work.N * Cout * Ho * Wo) * 4
+
+    def make_set(i):
+        X = X0.to("cuda") if i == 0 else X0.to("cuda").clone()
+        w = w0.to("cuda") if i == 0 else w0.to("cuda").clone()
+        Y = torch.empty((work.N, Cout, Ho, Wo), dtype=torch.float32, device="cuda")
+        return (X, w, Y)
+
+    def launch(st):
+        X, w, Y = st
+        rc = lib.conv_depthwise_fwd(X.data_ptr(), w.data_ptr(), None, Y.data_ptr(), work.N, work.C, work.H, work.W,
+                                    work.mult, work.KH, work.KW, work.stride, work.stride, work.pad, work.pad,
+                                    work.dil, work.dil, cf.CONV_DW_EXACT if exact else cf.CONV_DW_FAST,
+                                    torch.cuda.current_stream().cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"conv_depthwise_fwd failed: {cf.status_str(rc)}")
+
+    flops = 2.0 * work.N * Cout * Ho * Wo * work.KH * work.KW
+    return Runner(work.name, make_set, launch, set_bytes, mode), flops, set_bytes
+
+
+def measure(runner, steps, warmup, trials, reps_cap=None):
+    per_replay_target = 256
+    reps = max(1, per_replay_target // len(runner.sets))
+    if reps_cap:
+        reps = min(reps, reps_cap)
+    runner.capture(reps)
+    ms, n = runner.time(steps, warmup, trials)
+    return ms, n
+
+
+def cpu_baseline(work):
+    """The oracle, untuned, on a bounded sample of the headline workload: the
+    first images of the batch, sized to about 10-20 s of CPU work."""
+    import numpy as np
+    import oracle
+    import workloads as wl
+
+    threads = oracle.default_threads()
+    X, F = wl.dense_inputs(work)
+    Xf = X.float().numpy()
+    Ff = F.float().numpy()
+    t0 = time.perf_counter()
+    oracle.conv2d_nhwc(Xf[:1], Ff, threads=threads)
+    t1 = time.perf_counter() - t0
+    n_img = int(min(work.N, max(1, 15.0 // max(t1, 1e-3))))
+    t0 = time.perf_counter()
+    oracle.conv2d_nhwc(np.ascontiguousarray(Xf[:n_img]), Ff, threads=threads)
+    dt = time.perf_counter() - t0
+    Ho, Wo = work.H - work.KH + 1, work.W - work.KW + 1
+    flops = 2.0 * n_img * Ho * Wo * work.Cout * work.KH * work.KW * work.Cin
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {n_img} of {work.N} images of {work.name} (fp64-accumulate seven-loop C oracle, "
+                      f"OpenMP {threads} threads), {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this build runs on a single "
+              "MI355X and has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import convolution_forward_amd as cf
+    import workloads as wl
+
+    cf.load_library()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+
+    work = wl.DENSE_3X3_BF16
+    runner, flops, set_bytes = dense_runner(work, args.mode, "bf16")
+    ms, launches = measure(runner, args.steps, args.warmup, args.trials)
+    tflops = flops / (ms * 1e-3) / 1e12
+    gbs = set_bytes / (ms * 1e-3) / 1e9
+    variant = cf.dense_variant_for(runner.sets[0][0], runner.sets[0][1])
+    del runner
+    torch.cuda.empty_cache()
+
+    line = {
+        "metric": "conv fwd TFLOP/s (dense) and GB/s (depthwise), % of MI355X roofline",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": launches,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "dense3x3_bf16: NHWC X[32,58,58,64] bf16 * F[3,3,64,64] bf16 -> Y[32,56,56,64] bf16, "
+                               "fp32 accumulate, stride 1, no padding",
+                   "N": work.N, "H": work.H, "W": work.W, "Cin": work.Cin, "K": work.KH, "Cout": work.Cout,
+                   "out_dtype": "bf16", "cache_mode": args.mode,
+                   "buffer_sets": None, "kernel_variant": {1: "direct", 2: "mfma_implicit_gemm"}.get(variant)},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "algorithmic_bytes": set_bytes, "kernel_ms": ms,
+                     "mfma_tflops": round(tflops, 2), "mfma_peak": BF16_MFMA_PEAK_TFLOPS,
+                     "mfma_frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4)},
+    }
+    line["config"]["buffer_sets"] = max(1, math.ceil(COLD_BYTES / set_bytes)) if args.mode == "cold" else 1
+
+    secondary = []
+    if not args.no_secondary:
+        steps2 = max(200, args.steps // 4)
+        for name, make in [
+            ("dense1x1_bf16 (Y bf16)", lambda: dense_runner(wl.DENSE_1X1_BF16, args.mode, "bf16")),
+            ("dense1x1_f32", lambda: dense_runner(wl.DENSE_1X1_BF16, args.mode, "f32", "f32")),
+            ("dense3x3_bf16 (Y f32)", lambda: dense_runner(wl.DENSE_3X3_BF16, args.mode, "f32")),
+        ]:
+            r, fl, by = make()
+            m, n = measure(r, steps2, args.warmup, args.trials)
+            tf = fl / (m * 1e-3) / 1e12
+            peak = F32_MFMA_PEAK_TFLOPS if "f32" in name and "Y f32" not in name else BF16_MFMA_PEAK_TFLOPS
+            secondary.append({"workload": name, "ms": m, "launches": n, "TFLOP/s": round(tf, 2),
+                              "GB/s": round(by / (m * 1e-3) / 1e9, 1),
+                              "frac_hbm": round(by / (m * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                              "frac_mfma_peak": round(tf / peak, 4), "mfma_peak": peak})
+            del r
+            torch.cuda.empty_cache()
+        for work_dw, exact in [(wl.DW_5X5S2_EXACT, True)] + [(l, False) for l in wl.DW_SWEEP]:
+            r, fl, by = dw_runner(work_dw, args.mode, exact)
+            m, n = measure(r, steps2, args.warmup, args.trials)
+            gb = by / (m * 1e-3) / 1e9
+            secondary.append({"workload": work_dw.name + (" exact" if exact else " fast"), "ms": m, "launches": n,
+                              "GB/s": round(gb, 1), "frac_hbm": round(gb / HBM_PEAK_GBS, 4),
+                              "GFLOP/s": round(fl / (m * 1e-3) / 1e9, 1)})
+            del r
+            torch.cuda.empty_cache()
+    line["secondary"] = secondary
+
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(work)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

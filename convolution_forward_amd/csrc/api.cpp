@@ -1,0 +1,339 @@
+// C ABI of the convolution library: argument validation, output shapes,
+// variant choice and launch. Every argument error is returned before the
+// first HIP call; kernels are enqueued on the caller's stream and nothing is
+// allocated or synchronised here.
+#include <limits.h>
+#include <stdint.h>
+
+#include "internal.h"
+
+using namespace convfwd;
+
+namespace {
+
+bool dtype_known(conv_dtype d) { return d == CONV_F32 || d == CONV_BF16; }
+
+int64_t dtype_size(conv_dtype d) { return d == CONV_BF16 ? 2 : 4; }
+
+// Half-open byte range [lo, hi) touched by a strided 4-D tensor with
+// non-negative strides.
+struct Range {
+    uintptr_t lo, hi;
+};
+
+Range strided_range(const void *base, const int64_t *dims, const int64_t *strides, int64_t esize)
+{
+    int64_t last = 0;
+    for (int d = 0; d < 4; ++d)
+        last += (dims[d] - 1) * strides[d];
+    uintptr_t lo = (uintptr_t)base;
+    return Range{lo, lo + (uintptr_t)((last + 1) * esize)};
+}
+
+Range flat_range(const void *base, int64_t bytes)
+{
+    uintptr_t lo = (uintptr_t)base;
+    return Range{lo, lo + (uintptr_t)bytes};
+}
+
+bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+// Products of sizes must stay far from int64 overflow; every size here is an
+// int, so four of them fit, but stride arithmetic is checked separately.
+bool stride_ok(int64_t s) { return s >= 0 && s <= (int64_t(1) << 40); }
+
+// Shape, dtype and layout checks (no pointer checks); fills p except pointers.
+conv_status check_dense_shape(const int64_t *x_strides, const int64_t *y_strides, int N, int H, int W,
+                              int Cin, int KH, int KW, int Cout, conv_dtype x_dtype, conv_dtype y_dtype,
+                              DenseProblem *p)
+{
+    if (N <= 0 || H <= 0 || W <= 0 || Cin <= 0 || KH <= 0 || KW <= 0 || Cout <= 0)
+        return CONV_ERR_NONPOSITIVE;
+    if (KH > H || KW > W)
+        return CONV_ERR_SHAPE;
+    if (!dtype_known(x_dtype) || !dtype_known(y_dtype))
+        return CONV_ERR_DTYPE;
+    if (x_dtype == CONV_F32 && y_dtype == CONV_BF16)
+        return CONV_ERR_DTYPE;
+    const int Ho = H - KH + 1, Wo = W - KW + 1;
+
+    int64_t xs[4], ys[4];
+    if (x_strides) {
+        for (int d = 0; d < 4; ++d) {
+            if (!stride_ok(x_strides[d]))
+                return CONV_ERR_LAYOUT;
+            xs[d] = x_strides[d];
+        }
+        if (xs[3] != 1)
+            return CONV_ERR_LAYOUT;
+    } else {
+        xs[3] = 1;
+        xs[2] = Cin;
+        xs[1] = (int64_t)W * Cin;
+        xs[0] = (int64_t)H * W * Cin;
+    }
+    if (y_strides) {
+        for (int d = 0; d < 4; ++d) {
+            if (!stride_ok(y_strides[d]))
+                return CONV_ERR_LAYOUT;
+            ys[d] = y_strides[d];
+        }
+        // No self-overlap: each coarser axis steps past the whole extent of the finer ones.
+        const int64_t pix = Cout;
+        const int64_t row = (int64_t)(Wo - 1) * ys[2] + pix;
+        const int64_t img = (int64_t)(Ho - 1) * ys[1] + row;
+        if (ys[3] != 1 || ys[2] < pix || ys[1] < row || (N > 1 && ys[0] < img))
+            return CONV_ERR_LAYOUT;
+    } else {
+        ys[3] = 1;
+        ys[2] = Cout;
+        ys[1] = (int64_t)Wo * Cout;
+        ys[0] = (int64_t)Ho * Wo * Cout;
+    }
+
+    p->X = nullptr;
+    p->F = nullptr;
+    p->bias = nullptr;
+    p->Y = nullptr;
+    for (int d = 0; d < 4; ++d) {
+        p->xs[d] = xs[d];
+        p->ys[d] = ys[d];
+    }
+    p->N = N;
+    p->H = H;
+    p->W = W;
+    p->Cin = Cin;
+    p->KH = KH;
+    p->KW = KW;
+    p->Cout = Cout;
+    p->Ho = Ho;
+    p->Wo = Wo;
+    p->xdt = x_dtype;
+    p->ydt = y_dtype;
+    return CONV_OK;
+}
+
+conv_status validate_dense(const void *X, const int64_t *x_strides, const void *F, const float *bias,
+                           void *Y, const int64_t *y_strides, int N, int H, int W, int Cin, int KH,
+                           int KW, int Cout, conv_dtype x_dtype, conv_dtype y_dtype, DenseProblem *p)
+{
+    if (!X || !F || !Y)
+        return CONV_ERR_NULL;
+    conv_status st = check_dense_shape(x_strides, y_strides, N, H, W, Cin, KH, KW, Cout, x_dtype, y_dtype, p);
+    if (st != CONV_OK)
+        return st;
+    const int64_t xdims[4] = {N, H, W, Cin};
+    const int64_t ydims[4] = {N, p->Ho, p->Wo, Cout};
+    const Range ry = strided_range(Y, ydims, p->ys, dtype_size(y_dtype));
+    if (overlaps(ry, strided_range(X, xdims, p->xs, dtype_size(x_dtype))) ||
+        overlaps(ry, flat_range(F, (int64_t)KH * KW * Cin * Cout * dtype_size(x_dtype))) ||
+        (bias && overlaps(ry, flat_range(bias, (int64_t)Cout * 4))))
+        return CONV_ERR_ALIAS;
+    p->X = X;
+    p->F = F;
+    p->bias = bias;
+    p->Y = Y;
+    return CONV_OK;
+}
+
+int dense_auto(const DenseProblem &p) { return dense_tiled_supports(p) ? CONV_VARIANT_TILED : CONV_VARIANT_DIRECT; }
+
+// Shape and mode checks (no pointer checks); fills p except pointers.
+conv_status check_dw_shape(int N, int C, int H, int W, int mult, int KH, int KW, int sh, int sw, int ph, int pw,
+                           int dh, int dw, conv_dw_mode mode, DwProblem *p)
+{
+    if (N <= 0 || C <= 0 || H <= 0 || W <= 0 || mult <= 0 || KH <= 0 || KW <= 0 || sh < 1 || sw < 1 ||
+        dh < 1 || dw < 1 || ph < 0 || pw < 0)
+        return CONV_ERR_NONPOSITIVE;
+    if (mode != CONV_DW_EXACT && mode != CONV_DW_FAST)
+        return CONV_ERR_UNSUPPORTED;
+    const int64_t Ho = conv_out_size(H, KH, sh, ph, dh);
+    const int64_t Wo = conv_out_size(W, KW, sw, pw, dw);
+    if (Ho <= 0 || Wo <= 0)
+        return CONV_ERR_SHAPE;
+    if ((int64_t)C * mult > INT_MAX)
+        return CONV_ERR_UNSUPPORTED;
+    p->X = nullptr;
+    p->w = nullptr;
+    p->bias = nullptr;
+    p->Y = nullptr;
+    p->N = N;
+    p->C = C;
+    p->H = H;
+    p->W = W;
+    p->mult = mult;
+    p->KH = KH;
+    p->KW = KW;
+    p->sh = sh;
+    p->sw = sw;
+    p->ph = ph;
+    p->pw = pw;
+    p->dh = dh;
+    p->dw = dw;
+    p->Ho = (int)Ho;
+    p->Wo = (int)Wo;
+    p->mode = mode;
+    return CONV_OK;
+}
+
+conv_status validate_dw(const float *X, const float *w, const float *bias, float *Y, int N, int C, int H,
+                        int W, int mult, int KH, int KW, int sh, int sw, int ph, int pw, int dh, int dw,
+                        conv_dw_mode mode, DwProblem *p)
+{
+    if (!X || !w || !Y)
+        return CONV_ERR_NULL;
+    conv_status st = check_dw_shape(N, C, H, W, mult, KH, KW, sh, sw, ph, pw, dh, dw, mode, p);
+    if (st != CONV_OK)
+        return st;
+    const int64_t Cout = (int64_t)C * mult;
+    const Range ry = flat_range(Y, (int64_t)N * Cout * p->Ho * p->Wo * 4);
+    if (overlaps(ry, flat_range(X, (int64_t)N * C * H * W * 4)) ||
+        overlaps(ry, flat_range(w, Cout * KH * KW * 4)) || (bias && overlaps(ry, flat_range(bias, Cout * 4))))
+        return CONV_ERR_ALIAS;
+    p->X = X;
+    p->w = w;
+    p->bias = bias;
+    p->Y = Y;
+    return CONV_OK;
+}
+
+int dw_auto(const DwProblem &p) { return dw_tiled_supports(p) ? CONV_VARIANT_TILED : CONV_VARIANT_DIRECT; }
+
+conv_status launched(hipError_t e)
+{
+    if (e != hipSuccess)
+        return CONV_ERR_HIP;
+    return hipGetLastError() == hipSuccess ? CONV_OK : CONV_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t conv_out_size(int64_t in, int k, int stride, int pad, int dil)
+{
+    if (in <= 0 || k <= 0 || stride <= 0 || pad < 0 || dil <= 0)
+        return 0;
+    const int64_t eff = (int64_t)dil * (k - 1) + 1;
+    const int64_t span = in + 2 * (int64_t)pad - eff;
+    if (span < 0)
+        return 0;
+    return span / stride + 1;
+}
+
+const char *conv_status_str(conv_status s)
+{
+    switch (s) {
+    case CONV_OK: return "ok";
+    case CONV_ERR_NULL: return "a required pointer is NULL";
+    case CONV_ERR_NONPOSITIVE: return "sizes must be positive, strides and dilations >= 1, padding >= 0";
+    case CONV_ERR_SHAPE: return "the filter does not fit the input: no output position";
+    case CONV_ERR_DTYPE: return "unsupported dtype combination";
+    case CONV_ERR_LAYOUT: return "unsupported memory layout (channel stride must be 1, output must not overlap itself)";
+    case CONV_ERR_ALIAS: return "the output overlaps an input";
+    case CONV_ERR_UNSUPPORTED: return "arguments outside what this kernel handles";
+    case CONV_ERR_HIP: return "HIP runtime error at launch";
+    }
+    return "unknown status";
+}
+
+conv_status conv2d_nhwc_fwd_variant(const void *X, const int64_t *x_strides, const void *F,
+                                    const float *bias, void *Y, const int64_t *y_strides, int N, int H,
+                                    int W, int Cin, int KH, int KW, int Cout, conv_dtype x_dtype,
+                                    conv_dtype y_dtype, int variant, void *stream)
+{
+    DenseProblem p;
+    conv_status st = validate_dense(X, x_strides, F, bias, Y, y_strides, N, H, W, Cin, KH, KW, Cout, x_dtype,
+                                    y_dtype, &p);
+    if (st != CONV_OK)
+        return st;
+    if (variant == CONV_VARIANT_AUTO)
+        variant = dense_auto(p);
+    hipStream_t s = (hipStream_t)stream;
+    switch (variant) {
+    case CONV_VARIANT_DIRECT:
+        return launched(launch_dense_direct(p, s));
+    case CONV_VARIANT_TILED:
+        if (!dense_tiled_supports(p))
+            return CONV_ERR_UNSUPPORTED;
+        return launched(launch_dense_tiled(p, s));
+    default:
+        return CONV_ERR_UNSUPPORTED;
+    }
+}
+
+conv_status conv2d_nhwc_fwd(const void *X, const int64_t *x_strides, const void *F, const float *bias,
+                            void *Y, const int64_t *y_strides, int N, int H, int W, int Cin, int KH,
+                            int KW, int Cout, conv_dtype x_dtype, conv_dtype y_dtype, void *stream)
+{
+    return conv2d_nhwc_fwd_variant(X, x_strides, F, bias, Y, y_strides, N, H, W, Cin, KH, KW, Cout, x_dtype,
+                                   y_dtype, CONV_VARIANT_AUTO, stream);
+}
+
+int conv2d_nhwc_auto_variant(const int64_t *x_strides, const void *X, int N, int H, int W, int Cin, int KH,
+                             int KW, int Cout, conv_dtype x_dtype, conv_dtype y_dtype)
+{
+    DenseProblem p;
+    if (check_dense_shape(x_strides, nullptr, N, H, W, Cin, KH, KW, Cout, x_dtype, y_dtype, &p) != CONV_OK)
+        return -1;
+    p.X = X;    // only its alignment is looked at
+    return dense_auto(p);
+}
+
+conv_status conv_depthwise_fwd_variant(const float *X, const float *w, const float *bias, float *Y, int N,
+                                       int C, int H, int W, int multiplier, int KH, int KW, int stride_h,
+                                       int stride_w, int pad_h, int pad_w, int dil_h, int dil_w,
+                                       conv_dw_mode mode, int variant, void *stream)
+{
+    DwProblem p;
+    conv_status st = validate_dw(X, w, bias, Y, N, C, H, W, multiplier, KH, KW, stride_h, stride_w, pad_h, pad_w,
+                                 dil_h, dil_w, mode, &p);
+    if (st != CONV_OK)
+        return st;
+    if (variant == CONV_VARIANT_AUTO)
+        variant = dw_auto(p);
+    hipStream_t s = (hipStream_t)stream;
+    switch (variant) {
+    case CONV_VARIANT_DIRECT:
+        return launched(launch_dw_direct(p, s));
+    case CONV_VARIANT_TILED:
+        if (!dw_tiled_supports(p))
+            return CONV_ERR_UNSUPPORTED;
+        return launched(launch_dw_tiled(p, s));
+    default:
+        return CONV_ERR_UNSUPPORTED;
+    }
+}
+
+conv_status conv_depthwise_fwd(const float *X, const float *w, const float *bias, float *Y, int N, int C, int H,
+                               int W, int multiplier, int KH, int KW, int stride_h, int stride_w, int pad_h,
+                               int pad_w, int dil_h, int dil_w, conv_dw_mode mode, void *stream)
+{
+    return conv_depthwise_fwd_variant(X, w, bias, Y, N, C, H, W, multiplier, KH, KW, stride_h, stride_w, pad_h,
+                                      pad_w, dil_h, dil_w, mode, CONV_VARIANT_AUTO, stream);
+}
+
+int conv_depthwise_auto_variant(int N, int C, int H, int W, int multiplier, int KH, int KW, int stride_h,
+                                int stride_w, int pad_h, int pad_w, int dil_h, int dil_w)
+{
+    DwProblem p;
+    if (check_dw_shape(N, C, H, W, multiplier, KH, KW, stride_h, stride_w, pad_h, pad_w, dil_h, dil_w,
+                       CONV_DW_EXACT, &p) != CONV_OK)
+        return -1;
+    return dw_auto(p);
+}
+
+conv_status conv_copy_bytes(const void *src, void *dst, int64_t bytes, void *stream)
+{
+    if (!src || !dst)
+        return CONV_ERR_NULL;
+    if (bytes < 0)
+        return CONV_ERR_NONPOSITIVE;
+    if (overlaps(flat_range(src, bytes), flat_range(dst, bytes)))
+        return CONV_ERR_ALIAS;
+    if (bytes == 0)
+        return CONV_OK;
+    return launched(launch_copy_bytes(src, dst, bytes, (hipStream_t)stream));
+}
+
+}  // extern "C"

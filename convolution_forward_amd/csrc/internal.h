@@ -1,0 +1,47 @@
+// Internal declarations shared by the host dispatcher and the kernel files.
+// Nothing here is part of the public ABI (include/convfwd.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "convfwd.h"
+
+namespace convfwd {
+
+// A validated dense problem: NHWC X with element strides, KKIO F, NHWC Y.
+struct DenseProblem {
+    const void *X;
+    int64_t xs[4];
+    const void *F;
+    const float *bias;
+    void *Y;
+    int64_t ys[4];
+    int N, H, W, Cin, KH, KW, Cout, Ho, Wo;
+    conv_dtype xdt, ydt;
+};
+
+// A validated depthwise problem: contiguous NCHW X, [C*mult,KH,KW] w, NCHW Y.
+struct DwProblem {
+    const float *X;
+    const float *w;
+    const float *bias;
+    float *Y;
+    int N, C, H, W, mult, KH, KW, sh, sw, ph, pw, dh, dw, Ho, Wo;
+    conv_dw_mode mode;
+};
+
+// Dense kernels.
+hipError_t launch_dense_direct(const DenseProblem &p, hipStream_t s);
+bool dense_tiled_supports(const DenseProblem &p);
+hipError_t launch_dense_tiled(const DenseProblem &p, hipStream_t s);
+
+// Depthwise kernels.
+hipError_t launch_dw_direct(const DwProblem &p, hipStream_t s);
+bool dw_tiled_supports(const DwProblem &p);
+hipError_t launch_dw_tiled(const DwProblem &p, hipStream_t s);
+
+// Streaming copy used for bandwidth / counter calibration.
+hipError_t launch_copy_bytes(const void *src, void *dst, int64_t bytes, hipStream_t s);
+
+}  // namespace convfwd

@@ -1,0 +1,185 @@
+/*
+ * convfwd -- forward 2D convolution on AMD Instinct MI355X (gfx950).
+ *
+ * A C ABI over hand-written HIP kernels. Every argument is a plain pointer or
+ * integer; device buffers are owned by the caller. The library never
+ * allocates device memory, keeps no global state and never synchronises: each
+ * call validates its arguments on the host, then enqueues kernels on the
+ * caller's stream and returns.
+ *
+ * Two operators:
+ *
+ *  - Dense NHWC cross-correlation, as fixed by "CMU DLSys Lecture 14:
+ *    Convolutional Network Implementation", section 1 (the index contract):
+ *    Y[n,y,x,o] = sum over i<KH, j<KW, c<Cin of X[n,y+i,x+j,c] * F[i,j,c,o],
+ *    no flip, unit stride, no padding, Ho = H-KH+1, Wo = W-KW+1. The lecture
+ *    uses square filters; KH and KW are separate here so that 1D filters
+ *    (KH = 1) from "Convolution Is Wx+b Moving Across a Signal" run too.
+ *
+ *  - Depthwise convolution, as fixed by "Depthwise convolution" (onemodel
+ *    docs), section "What each output is": one input channel per group,
+ *    Cout = C * multiplier, output channel oc reads input channel
+ *    oc / multiplier; stride, symmetric zero padding and dilation per axis;
+ *    taps summed row-major starting from +0; exact or fast rounding.
+ *
+ * Return values: every function that can fail returns a conv_status. All
+ * argument errors are detected before any HIP call, and then nothing is
+ * written and nothing is enqueued. CONV_ERR_HIP reports a failed launch.
+ */
+#ifndef CONVFWD_H
+#define CONVFWD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Exported symbols; everything else in the library is hidden. */
+#if defined(__GNUC__) || defined(__clang__)
+#define CONVFWD_API __attribute__((visibility("default")))
+#else
+#define CONVFWD_API
+#endif
+
+typedef enum conv_status {
+    CONV_OK = 0,
+    CONV_ERR_NULL = 1,          /* a required pointer is NULL */
+    CONV_ERR_NONPOSITIVE = 2,   /* a size <= 0, stride or dilation < 1, or padding < 0 */
+    CONV_ERR_SHAPE = 3,         /* the filter does not fit (no output position) */
+    CONV_ERR_DTYPE = 4,         /* unknown dtype, or bf16 output requested from fp32 input */
+    CONV_ERR_LAYOUT = 5,        /* a stride the operator cannot address (see each call) */
+    CONV_ERR_ALIAS = 6,         /* the output's address range overlaps an input's */
+    CONV_ERR_UNSUPPORTED = 7,   /* valid arguments outside what the (forced) kernel handles */
+    CONV_ERR_HIP = 8            /* the HIP runtime reported an error at launch */
+} conv_status;
+
+typedef enum conv_dtype {
+    CONV_F32 = 0,   /* IEEE binary32 */
+    CONV_BF16 = 1   /* bfloat16 (upper half of a binary32) */
+} conv_dtype;
+
+typedef enum conv_dw_mode {
+    CONV_DW_EXACT = 0,  /* round the product, then round the sum; NaN -> 0x7FC00000 */
+    CONV_DW_FAST = 1    /* one fused multiply-add per tap */
+} conv_dw_mode;
+
+/* Kernel variants. CONV_VARIANT_AUTO picks by shape; the others force one
+ * kernel family and return CONV_ERR_UNSUPPORTED if it cannot take the shape.
+ * Every variant computes the same contract; dense variants may differ in
+ * fp32 accumulation order only, depthwise variants give identical bits. */
+enum {
+    CONV_VARIANT_AUTO = 0,
+    CONV_VARIANT_DIRECT = 1,     /* one thread per output, any legal shape */
+    CONV_VARIANT_TILED = 2       /* dense: MFMA implicit GEMM; depthwise: LDS-staged tiles */
+};
+
+/*
+ * conv2d_nhwc_fwd -- dense forward cross-correlation.
+ *
+ * Contract: "CMU DLSys Lecture 14", section 1 (above); the filter is used as
+ * the matrix F.reshape(KH*KW*Cin, Cout) with rows in (i,j,c) order (section 5),
+ * but no patch matrix is ever built: patches are gathered on the fly.
+ *
+ *   X          device pointer, logical NHWC [N,H,W,Cin], dtype x_dtype.
+ *   x_strides  host array of 4 element strides (n,h,w,c), or NULL for the
+ *              contiguous layout. Like the lecture's strided patch view, any
+ *              non-negative strides are accepted as long as the channel
+ *              stride is 1 (CONV_ERR_LAYOUT otherwise); X may be a view.
+ *   F          device pointer, contiguous [KH,KW,Cin,Cout] (KKIO), dtype x_dtype.
+ *   bias       device pointer to Cout fp32 values added to every output, or NULL.
+ *   Y          device pointer, logical NHWC [N,Ho,Wo,Cout], dtype y_dtype.
+ *   y_strides  host array of 4 element strides, or NULL for contiguous. The
+ *              channel stride must be 1 and the layout must not overlap
+ *              itself (sW >= Cout, sH >= (Wo-1)*sW + Cout,
+ *              sN >= (Ho-1)*sH + (Wo-1)*sW + Cout); CONV_ERR_LAYOUT otherwise.
+ *   x_dtype    CONV_F32 or CONV_BF16 (X and F share it).
+ *   y_dtype    CONV_F32, or CONV_BF16 when x_dtype is CONV_BF16. Accumulation
+ *              is fp32; bf16 output is rounded to nearest-even once at the end.
+ *   stream     a hipStream_t (NULL = the default stream).
+ *
+ * Errors: CONV_ERR_NULL (X, F or Y NULL), CONV_ERR_NONPOSITIVE (any size
+ * <= 0), CONV_ERR_SHAPE (KH > H or KW > W), CONV_ERR_DTYPE, CONV_ERR_LAYOUT,
+ * CONV_ERR_ALIAS (Y's byte range overlaps X, F or bias), CONV_ERR_HIP.
+ * Y is fully overwritten on success; nothing accumulates into it.
+ */
+CONVFWD_API conv_status conv2d_nhwc_fwd(const void *X, const int64_t *x_strides, const void *F, const float *bias,
+                            void *Y, const int64_t *y_strides, int N, int H, int W, int Cin, int KH,
+                            int KW, int Cout, conv_dtype x_dtype, conv_dtype y_dtype, void *stream);
+
+/* conv2d_nhwc_fwd with a forced kernel variant (CONV_VARIANT_*). The MFMA
+ * variant needs bf16 or fp32 X with a 16-byte-aligned base and 16-byte
+ * aligned pixel strides for bf16 (8 channels) or fp32 (4 channels), and
+ * Cin and Cout that are multiples of 8 (bf16) or 4 (fp32); otherwise it
+ * returns CONV_ERR_UNSUPPORTED. */
+CONVFWD_API conv_status conv2d_nhwc_fwd_variant(const void *X, const int64_t *x_strides, const void *F,
+                                    const float *bias, void *Y, const int64_t *y_strides, int N, int H,
+                                    int W, int Cin, int KH, int KW, int Cout, conv_dtype x_dtype,
+                                    conv_dtype y_dtype, int variant, void *stream);
+
+/*
+ * conv_depthwise_fwd -- depthwise forward convolution, fp32, NCHW planes.
+ *
+ * Contract: "Depthwise convolution" (onemodel docs), section "What each
+ * output is". For output plane (n, oc), input plane (n, oc / multiplier):
+ *   acc = +0; for ky < KH: for kx < KW:
+ *     acc = acc + w[oc,ky,kx] * xpad[oy*stride_h + ky*dil_h, ox*stride_w + kx*dil_w]
+ * where xpad is the input plane with pad_h / pad_w rows / columns of real
+ * zeros on each side (a padding tap is a multiplication by +0, so an
+ * infinite or NaN weight there yields NaN). Output size per axis follows
+ * conv_out_size.
+ *   mode CONV_DW_EXACT: each product and each sum rounded to fp32 separately,
+ *        in the row-major order above; a NaN result becomes 0x7FC00000.
+ *   mode CONV_DW_FAST: acc = fma(w, x, acc) per tap, same order.
+ *   bias (nullable, Cout fp32): one rounded addition per output after the
+ *        taps (and before the NaN rewrite of exact mode).
+ * Results are bit-identical across kernel variants and launches.
+ *
+ *   X  device, contiguous [N,C,H,W] fp32.   w  device, contiguous [C*multiplier,KH,KW] fp32.
+ *   Y  device, contiguous [N,C*multiplier,Ho,Wo] fp32, fully overwritten.
+ *
+ * Errors: CONV_ERR_NULL (X, w or Y NULL), CONV_ERR_NONPOSITIVE (a size or
+ * multiplier <= 0, stride or dilation < 1, padding < 0), CONV_ERR_SHAPE (an
+ * output size <= 0), CONV_ERR_UNSUPPORTED (unknown mode, or a forced variant
+ * that cannot take the shape), CONV_ERR_ALIAS (Y overlaps X, w or bias),
+ * CONV_ERR_HIP.
+ */
+CONVFWD_API conv_status conv_depthwise_fwd(const float *X, const float *w, const float *bias, float *Y, int N, int C,
+                               int H, int W, int multiplier, int KH, int KW, int stride_h, int stride_w,
+                               int pad_h, int pad_w, int dil_h, int dil_w, conv_dw_mode mode,
+                               void *stream);
+
+/* conv_depthwise_fwd with a forced kernel variant (CONV_VARIANT_*). */
+CONVFWD_API conv_status conv_depthwise_fwd_variant(const float *X, const float *w, const float *bias, float *Y, int N,
+                                       int C, int H, int W, int multiplier, int KH, int KW, int stride_h,
+                                       int stride_w, int pad_h, int pad_w, int dil_h, int dil_w,
+                                       conv_dw_mode mode, int variant, void *stream);
+
+/* Which variant CONV_VARIANT_AUTO would launch for these dense / depthwise
+ * arguments (a CONV_VARIANT_* value), or -1 if the arguments are invalid.
+ * Host-only; makes no HIP call. */
+CONVFWD_API int conv2d_nhwc_auto_variant(const int64_t *x_strides, const void *X, int N, int H, int W, int Cin,
+                             int KH, int KW, int Cout, conv_dtype x_dtype, conv_dtype y_dtype);
+CONVFWD_API int conv_depthwise_auto_variant(int N, int C, int H, int W, int multiplier, int KH, int KW, int stride_h,
+                                int stride_w, int pad_h, int pad_w, int dil_h, int dil_w);
+
+/* Output size along one axis: floor((in + 2*pad - (dil*(k-1)+1)) / stride) + 1
+ * ("Convolution Is Wx+b Moving Across a Signal", section "Why 1D? Why 2D?").
+ * Returns a value <= 0 when no window fits or an argument is out of range. */
+CONVFWD_API int64_t conv_out_size(int64_t in, int k, int stride, int pad, int dil);
+
+/* Static, NUL-terminated description of a status code. */
+CONVFWD_API const char *conv_status_str(conv_status s);
+
+/* Copy `bytes` bytes from src to dst (device pointers, non-overlapping) with a
+ * plain streaming kernel on `stream`. It is not part of the convolution; it
+ * calibrates memory-traffic counters and the achievable HBM bandwidth.
+ * Errors: CONV_ERR_NULL, CONV_ERR_NONPOSITIVE (bytes < 0), CONV_ERR_ALIAS,
+ * CONV_ERR_HIP. bytes == 0 enqueues nothing. */
+CONVFWD_API conv_status conv_copy_bytes(const void *src, void *dst, int64_t bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CONVFWD_H */

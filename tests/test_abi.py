@@ -1,0 +1,161 @@
+"""The C ABI, checked without a GPU: the library loads, exports exactly what
+include/convfwd.h declares, and rejects every invalid argument before any HIP
+call (so these calls are safe on a machine with no GPU: fake, distinct device
+addresses are passed and never dereferenced)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import convolution_forward_amd as cf
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "convfwd.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(cf.LIB_PATH):
+        from convolution_forward_amd import build
+        build.build()
+    return cf.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"CONVFWD_API\s+[\w\s\*]+?\b(\w+)\s*\(", text)))
+
+
+def test_exports_match_header(lib):
+    names = declared_functions()
+    assert set(names) == set(cf.EXPORTED)
+    out = subprocess.run(["nm", "-D", "--defined-only", cf.LIB_PATH], capture_output=True, text=True, check=True)
+    exported = {line.split()[-1] for line in out.stdout.splitlines() if " T " in line}
+    assert exported == set(names), f"exported {sorted(exported)} vs declared {names}"
+    for n in names:
+        getattr(lib, n)
+
+
+def test_library_never_allocates_device_memory(lib):
+    """No hidden copy: the library imports no allocation or synchronisation API."""
+    out = subprocess.run(["nm", "-D", "--undefined-only", cf.LIB_PATH], capture_output=True, text=True, check=True)
+    undefined = {line.split()[-1] for line in out.stdout.splitlines()}
+    bad = [s for s in undefined if re.match(r"hip(Ext)?(Malloc|Free|MallocAsync|HostMalloc|MallocManaged|"
+                                              r"DeviceSynchronize|StreamSynchronize|Memcpy)", s)]
+    assert not bad, bad
+
+
+def test_status_strings(lib):
+    for s in range(9):
+        assert len(cf.status_str(s)) >= 2
+    assert cf.status_str(99) == "unknown status"
+
+
+def test_out_size(lib):
+    assert cf.out_size(5, 3) == 3                       # the pages' 1D example
+    assert cf.out_size(56, 5, 2, 2, 1) == 28
+    assert cf.out_size(112, 3, 2, 1, 1) == 56
+    assert cf.out_size(7, 5, 1, 2, 1) == 7
+    assert cf.out_size(3, 5) <= 0
+    assert cf.out_size(0, 1) <= 0 and cf.out_size(4, 1, 0) <= 0 and cf.out_size(4, 1, 1, -1) <= 0
+
+
+# Fake, widely separated device addresses: validation only compares them.
+XA, FA, BA, YA = 0x10000000, 0x20000000, 0x30000000, 0x40000000
+
+
+def dense(lib, X=XA, xs=None, F=FA, bias=None, Y=YA, ys=None, shape=(2, 8, 8, 3, 3, 3, 4), xdt=0, ydt=0,
+          variant=0):
+    N, H, W, Cin, KH, KW, Cout = shape
+    xs_arr = None if xs is None else (ctypes.c_int64 * 4)(*xs)
+    ys_arr = None if ys is None else (ctypes.c_int64 * 4)(*ys)
+    return lib.conv2d_nhwc_fwd_variant(X, xs_arr, F, bias, Y, ys_arr, N, H, W, Cin, KH, KW, Cout, xdt, ydt,
+                                       variant, None)
+
+
+def test_dense_errors(lib):
+    assert dense(lib, X=None) == cf.CONV_ERR_NULL
+    assert dense(lib, F=None) == cf.CONV_ERR_NULL
+    assert dense(lib, Y=None) == cf.CONV_ERR_NULL
+    for i in range(7):
+        shape = [2, 8, 8, 3, 3, 3, 4]
+        shape[i] = 0
+        assert dense(lib, shape=tuple(shape)) == cf.CONV_ERR_NONPOSITIVE
+        shape[i] = -1
+        assert dense(lib, shape=tuple(shape)) == cf.CONV_ERR_NONPOSITIVE
+    assert dense(lib, shape=(1, 2, 8, 3, 3, 3, 4)) == cf.CONV_ERR_SHAPE       # KH > H
+    assert dense(lib, shape=(1, 8, 2, 3, 3, 3, 4)) == cf.CONV_ERR_SHAPE       # KW > W
+    assert dense(lib, xdt=2) == cf.CONV_ERR_DTYPE
+    assert dense(lib, ydt=7) == cf.CONV_ERR_DTYPE
+    assert dense(lib, xdt=cf.CONV_F32, ydt=cf.CONV_BF16) == cf.CONV_ERR_DTYPE
+    assert dense(lib, xs=(192, 24, 3, 2)) == cf.CONV_ERR_LAYOUT               # channel stride != 1
+    assert dense(lib, xs=(192, -24, 3, 1)) == cf.CONV_ERR_LAYOUT              # negative stride
+    assert dense(lib, ys=(144, 24, 4, 2)) == cf.CONV_ERR_LAYOUT
+    assert dense(lib, ys=(144, 24, 3, 1)) == cf.CONV_ERR_LAYOUT               # pixels overlap (sW < Cout)
+    assert dense(lib, ys=(144, 20, 4, 1)) == cf.CONV_ERR_LAYOUT               # rows overlap
+    assert dense(lib, ys=(100, 24, 4, 1)) == cf.CONV_ERR_LAYOUT               # images overlap
+    # Y overlapping X (element 5 of X), F or bias.
+    assert dense(lib, Y=XA + 20) == cf.CONV_ERR_ALIAS
+    assert dense(lib, Y=FA - 8) == cf.CONV_ERR_ALIAS
+    assert dense(lib, bias=YA + 4) == cf.CONV_ERR_ALIAS
+    # X is read-only: overlapping X and F, or a zero stride in X, is legal.
+    assert dense(lib, F=XA + 4, variant=99) == cf.CONV_ERR_UNSUPPORTED
+    assert dense(lib, xs=(0, 24, 3, 1), variant=99) == cf.CONV_ERR_UNSUPPORTED
+    assert dense(lib, variant=99) == cf.CONV_ERR_UNSUPPORTED
+
+
+def dw(lib, X=XA, w=FA, bias=None, Y=YA, shape=(8, 72, 56, 56, 1, 5, 5, 2, 2, 2, 2, 1, 1), mode=0, variant=0):
+    return lib.conv_depthwise_fwd_variant(X, w, bias, Y, *shape, mode, variant, None)
+
+
+def test_depthwise_errors(lib):
+    assert dw(lib, X=None) == cf.CONV_ERR_NULL
+    assert dw(lib, w=None) == cf.CONV_ERR_NULL
+    assert dw(lib, Y=None) == cf.CONV_ERR_NULL
+    base = [8, 72, 56, 56, 1, 5, 5, 2, 2, 2, 2, 1, 1]
+    for i in range(7):                        # sizes, multiplier, KH, KW
+        s = list(base)
+        s[i] = 0
+        assert dw(lib, shape=tuple(s)) == cf.CONV_ERR_NONPOSITIVE
+    for i in (7, 8, 11, 12):                  # stride, dilation < 1
+        s = list(base)
+        s[i] = 0
+        assert dw(lib, shape=tuple(s)) == cf.CONV_ERR_NONPOSITIVE
+    for i in (9, 10):                         # padding < 0
+        s = list(base)
+        s[i] = -1
+        assert dw(lib, shape=tuple(s)) == cf.CONV_ERR_NONPOSITIVE
+    assert dw(lib, shape=(1, 1, 3, 3, 1, 5, 5, 1, 1, 0, 0, 1, 1)) == cf.CONV_ERR_SHAPE
+    assert dw(lib, shape=(1, 1, 7, 7, 1, 3, 3, 1, 1, 0, 0, 4, 1)) == cf.CONV_ERR_SHAPE   # dilated span 9 > 7
+    assert dw(lib, mode=2) == cf.CONV_ERR_UNSUPPORTED
+    assert dw(lib, Y=XA + 4096) == cf.CONV_ERR_ALIAS
+    assert dw(lib, bias=YA) == cf.CONV_ERR_ALIAS
+    assert dw(lib, w=YA + 8) == cf.CONV_ERR_ALIAS
+    assert dw(lib, variant=99) == cf.CONV_ERR_UNSUPPORTED
+
+
+def test_copy_errors(lib):
+    assert lib.conv_copy_bytes(None, YA, 16, None) == cf.CONV_ERR_NULL
+    assert lib.conv_copy_bytes(XA, YA, -1, None) == cf.CONV_ERR_NONPOSITIVE
+    assert lib.conv_copy_bytes(XA, XA + 8, 16, None) == cf.CONV_ERR_ALIAS
+    assert lib.conv_copy_bytes(XA, YA, 0, None) == cf.CONV_OK        # nothing enqueued
+
+
+def test_auto_variant_queries(lib):
+    assert lib.conv2d_nhwc_auto_variant(None, XA, 0, 8, 8, 3, 3, 3, 4, 0, 0) == -1
+    assert lib.conv2d_nhwc_auto_variant(None, XA, 2, 8, 8, 3, 3, 3, 4, 0, 0) in (cf.VARIANT_DIRECT, cf.VARIANT_TILED)
+    assert lib.conv_depthwise_auto_variant(1, 1, 3, 3, 1, 5, 5, 1, 1, 0, 0, 1, 1) == -1
+    v = lib.conv_depthwise_auto_variant(8, 72, 56, 56, 1, 5, 5, 2, 2, 2, 2, 1, 1)
+    assert v in (cf.VARIANT_DIRECT, cf.VARIANT_TILED)
+
+
+def test_binding_rejects_cpu_tensors(lib):
+    import torch
+    x = torch.zeros(1, 4, 4, 8)
+    f = torch.zeros(3, 3, 8, 8)
+    with pytest.raises(ValueError):
+        cf.conv2d_nhwc(x, f)
+    with pytest.raises(ValueError):
+        cf.conv_depthwise(torch.zeros(1, 2, 4, 4), torch.zeros(2, 3, 3))

@@ -1,0 +1,220 @@
+"""Dense conv2d parity on the GPU: the HIP path (through the C ABI) against
+the fp64 CPU oracle on identical seeded inputs.
+
+Tolerances: fp32 max relative error 1e-5 (relative to the largest output);
+bf16 inputs with fp32 accumulation 2e-2 relative to the output RMS; integer-
+valued inputs bitwise (every partial sum is an exact integer in fp32).
+"""
+import numpy as np
+import pytest
+import torch
+
+import convolution_forward_amd as cf
+import oracle
+import workloads as wl
+from conftest import golden
+from parity import BF16_RMS_REL, F32_MAX_REL, bf16_ulp_distance, bits, max_rel_err, rms_rel_err, to_f64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+VARIANTS = [cf.VARIANT_DIRECT, cf.VARIANT_TILED]
+
+
+def run(x, f, bias=None, out_dtype=None, variant=cf.VARIANT_AUTO, out=None):
+    y = cf.conv2d_nhwc(x.to(DEV) if not x.is_cuda else x, f.to(DEV), bias=None if bias is None else bias.to(DEV),
+                       out_dtype=out_dtype, variant=variant, out=out)
+    torch.cuda.synchronize()
+    return y
+
+
+def supported(x, f, variant, out_dtype=None):
+    """Whether a forced variant accepts the shape (UNSUPPORTED otherwise)."""
+    if variant != cf.VARIANT_TILED:
+        return True
+    xd = x.to(DEV)
+    return cf.dense_variant_for(xd, f, out_dtype) == cf.VARIANT_TILED
+
+
+# --- the pages' worked examples on the GPU -------------------------------------
+
+def test_gpu_lecture_arange_example():
+    g = golden("lecture14_arange_patches.json")
+    X = torch.arange(36, dtype=torch.float32).reshape(1, 6, 6, 1)
+    F = torch.arange(9, dtype=torch.float32).reshape(3, 3, 1, 1)
+    Y = run(X, F)
+    assert Y.cpu()[0, :, :, 0].tolist() == g["output"]
+
+
+def test_gpu_wxb_examples():
+    g1 = golden("wxb_1d_examples.json")
+    w = g1["window"]
+    Y = run(torch.tensor(w["x"], dtype=torch.float32).reshape(1, 1, -1, 1),
+            torch.tensor(w["k"], dtype=torch.float32).reshape(1, -1, 1, 1),
+            bias=torch.tensor([float(w["bias"])]))
+    assert Y.cpu().ravel().tolist() == w["y"]
+    t = g1["two_filters"]
+    Y = run(torch.tensor(t["x"], dtype=torch.float32).reshape(1, 1, -1, 1),
+            torch.tensor(t["K_taps_by_filters"], dtype=torch.float32).reshape(1, 3, 1, 2),
+            bias=torch.tensor(t["bias"], dtype=torch.float32))
+    assert Y.cpu()[0, 0].tolist() == t["y_positions_by_filters"]
+    g2 = golden("wxb_2d_examples.json")
+    s = g2["small"]
+    Y = run(torch.tensor(s["image"], dtype=torch.float32).reshape(1, 3, 3, 1),
+            torch.tensor(s["filter"], dtype=torch.float32).reshape(2, 2, 1, 1))
+    assert Y.cpu()[0, :, :, 0].tolist() == s["output"]
+    sb = g2["sobel"]
+    img = torch.zeros(6, 6)
+    img[:, 3:] = 1
+    F = torch.stack([torch.tensor(sb["gx"], dtype=torch.float32), torch.tensor(sb["gy"], dtype=torch.float32)], -1)
+    for dt in (torch.float32, torch.bfloat16):
+        Y = run(img.reshape(1, 6, 6, 1).to(dt), F.reshape(3, 3, 1, 2).to(dt), out_dtype=torch.float32)
+        assert Y.cpu()[0, :, :, 0].tolist() == sb["gx_output"]
+        assert Y.cpu()[0, :, :, 1].tolist() == sb["gy_output"]
+
+
+# --- the tiny fp32 workload, full tensor ---------------------------------------
+
+@pytest.mark.parametrize("variant", [cf.VARIANT_AUTO] + VARIANTS)
+def test_gpu_dense_tiny_f32(variant):
+    w = wl.DENSE_TINY_F32
+    X, F = wl.dense_inputs(w)
+    if not supported(X, F.to(DEV), variant):
+        pytest.skip("tiled variant does not take Cin=3")
+    ref = oracle.conv2d_nhwc(X, F)
+    Y = run(X, F, variant=variant)
+    assert tuple(Y.shape) == (2, 6, 6, 4)
+    assert max_rel_err(Y, ref) <= F32_MAX_REL
+
+
+# --- shapes spanning several tiles with ragged tails ---------------------------
+
+SHAPES = [  # N, H, W, Cin, K, Cout
+    (2, 17, 23, 64, 3, 64),
+    (1, 30, 9, 32, 3, 48),
+    (3, 12, 40, 16, 5, 24),
+    (2, 20, 19, 128, 1, 96),
+    (1, 8, 70, 8, 2, 8),
+    (2, 11, 13, 3, 3, 5),
+    (1, 7, 7, 40, 7, 16),          # filter spans the whole image
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_gpu_dense_shapes(shape, dtype, variant):
+    N, H, W, C, K, O = shape
+    seed = 1000 + SHAPES.index(shape)
+    X = wl.random_tensor((N, H, W, C), seed)
+    F = wl.random_tensor((K, K, C, O), seed + 1) * (1.0 / (K * K * C) ** 0.5)
+    if dtype == "bf16":
+        X, F = X.to(torch.bfloat16), F.to(torch.bfloat16)
+    if not supported(X, F.to(DEV), variant):
+        pytest.skip("shape outside the tiled variant")
+    ref = oracle.conv2d_nhwc(X, F)
+    Y = run(X, F, variant=variant, out_dtype=torch.float32)
+    if dtype == "f32":
+        assert max_rel_err(Y, ref) <= F32_MAX_REL
+    else:
+        assert rms_rel_err(Y, ref) <= 1e-3          # fp32 output: only accumulation order differs
+        Yb = run(X, F, variant=variant)
+        assert Yb.dtype == torch.bfloat16
+        assert rms_rel_err(Yb, ref) <= BF16_RMS_REL
+        assert bf16_ulp_distance(Yb, ref) <= 1
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_gpu_dense_integer_bitwise(variant):
+    """Integer-valued inputs keep every partial sum exact, so any accumulation
+    order must reproduce the oracle bit for bit."""
+    X = wl.random_tensor((2, 13, 21, 64), 77, integer_range=4)
+    F = wl.random_tensor((3, 3, 64, 32), 78, integer_range=4)
+    ref = oracle.conv2d_nhwc(X, F)
+    assert np.max(np.abs(ref)) < 2 ** 24
+    for dt in (torch.float32, torch.bfloat16):
+        if not supported(X.to(dt), F.to(dt).to(DEV), variant):
+            continue
+        Y = run(X.to(dt), F.to(dt), variant=variant, out_dtype=torch.float32)
+        np.testing.assert_array_equal(to_f64(Y), ref)
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_gpu_dense_bias_and_views(variant):
+    """Bias in the epilogue; X as a non-contiguous view (channel stride 1) and
+    Y written through strides into a larger buffer, untouched elsewhere."""
+    base = wl.random_tensor((2, 14, 20, 80), 91).to(torch.bfloat16).to(DEV)
+    X = base[:, 1:13, 2:18, 8:72]                    # [2,12,16,64], strided
+    F = (wl.random_tensor((3, 3, 64, 32), 92) * 0.05).to(torch.bfloat16)
+    b = wl.random_tensor((32,), 93)
+    if not supported(X, F.to(DEV), variant):
+        pytest.skip("view outside the tiled variant")
+    ref = oracle.conv2d_nhwc(X.cpu(), F, bias=b)
+    big = torch.full((2, 12, 16, 48), float("nan"), dtype=torch.float32, device=DEV)
+    Yv = big[:, 1:11, 1:15, 8:40]
+    run(X, F, bias=b, variant=variant, out=Yv)
+    assert rms_rel_err(Yv, ref) <= 1e-3
+    mask = torch.ones_like(big, dtype=torch.bool)
+    mask[:, 1:11, 1:15, 8:40] = False
+    assert torch.isnan(big[mask]).all()
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_gpu_dense_write_coverage_and_determinism(variant):
+    X = wl.random_tensor((3, 19, 27, 32), 55).to(torch.bfloat16)
+    F = (wl.random_tensor((3, 3, 32, 40), 56) * 0.1).to(torch.bfloat16)
+    if not supported(X, F.to(DEV), variant):
+        pytest.skip("outside the tiled variant")
+    out = torch.full((3, 17, 25, 40), float("nan"), dtype=torch.bfloat16, device=DEV)
+    Y1 = run(X, F, variant=variant, out=out).clone()
+    assert not torch.isnan(Y1).any()
+    Y2 = run(X, F, variant=variant)
+    assert torch.equal(Y1.view(torch.int16), Y2.view(torch.int16))
+
+
+# --- the full-size workloads, in the launch configuration the benchmark uses ---
+
+def sample_indices(shape, n, seed):
+    """Random flat output indices plus every output of the first and last
+    rows, columns and channels' corners (borders of the halo)."""
+    N, Ho, Wo, O = shape
+    rng = np.random.default_rng(seed)
+    idx = set(rng.integers(0, N * Ho * Wo * O, size=n).tolist())
+    for nn in (0, N - 1):
+        for y in (0, Ho - 1):
+            for x in range(Wo):
+                for o in (0, O - 1):
+                    idx.add(((nn * Ho + y) * Wo + x) * O + o)
+        for y in range(Ho):
+            for x in (0, Wo - 1):
+                for o in range(O):
+                    idx.add(((nn * Ho + y) * Wo + x) * O + o)
+    return np.array(sorted(idx), dtype=np.int64)
+
+
+@pytest.mark.parametrize("work", [wl.DENSE_3X3_BF16, wl.DENSE_1X1_BF16], ids=lambda w: w.name)
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32], ids=["ybf16", "yf32"])
+def test_gpu_dense_full_size_sampled(work, out_dtype):
+    X, F = wl.dense_inputs(work)
+    Y = run(X, F, out_dtype=out_dtype)
+    shape = (work.N, work.H - work.KH + 1, work.W - work.KW + 1, work.Cout)
+    assert tuple(Y.shape) == shape
+    idx = sample_indices(shape, 20000, work.seed)
+    ref = oracle.conv2d_nhwc_at(X, F, idx)
+    got = Y.reshape(-1)[torch.from_numpy(idx).to(DEV)]
+    if out_dtype == torch.bfloat16:
+        assert rms_rel_err(got, ref) <= BF16_RMS_REL
+        assert bf16_ulp_distance(got, ref) <= 1
+    else:
+        assert rms_rel_err(got, ref) <= 1e-4
+    assert torch.isfinite(Y).all()
+
+
+def test_gpu_dense_1x1_f32_full_size_sampled():
+    work = wl.DENSE_1X1_BF16
+    X, F = wl.dense_inputs(work, dtype="f32")
+    Y = run(X, F)
+    shape = (work.N, work.H, work.W, work.Cout)
+    idx = sample_indices(shape, 20000, 7)
+    ref = oracle.conv2d_nhwc_at(X, F, idx)
+    got = Y.reshape(-1)[torch.from_numpy(idx).to(DEV)]
+    assert max_rel_err(got, ref) <= F32_MAX_REL
