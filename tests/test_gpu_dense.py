@@ -139,6 +139,22 @@ def test_gpu_dense_integer_bitwise(variant):
 
 
 @pytest.mark.parametrize("variant", VARIANTS)
+def test_gpu_dense_bf16_output_rounds_to_nearest_even(variant):
+    """Integer sums are exact in fp32, so the bf16 output must be exactly the
+    exact sum rounded to nearest-even (torch's CPU fp32->bf16 conversion).
+    Values above 256 need rounding; truncation or ties-away would differ."""
+    X = wl.random_tensor((2, 9, 30, 64), 81, integer_range=6).to(torch.bfloat16)
+    F = wl.random_tensor((3, 3, 64, 32), 82, integer_range=6).to(torch.bfloat16)
+    if not supported(X, F.to(DEV), variant):
+        pytest.skip("outside the tiled variant")
+    ref = oracle.conv2d_nhwc(X, F)
+    assert np.max(np.abs(ref)) < 2 ** 24 and np.mean(np.abs(ref) > 256) > 0.3
+    expect = torch.from_numpy(ref.astype(np.float32)).to(torch.bfloat16)
+    Y = run(X, F, variant=variant)
+    assert torch.equal(Y.cpu().view(torch.int16), expect.view(torch.int16))
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
 def test_gpu_dense_bias_and_views(variant):
     """Bias in the epilogue; X as a non-contiguous view (channel stride 1) and
     Y written through strides into a larger buffer, untouched elsewhere."""
