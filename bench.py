@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--trials", type=int, default=3)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also time the plain copy kernel (HBM bandwidth context, counter calibration)")
     return ap.parse_args()
 
 
@@ -279,6 +281,26 @@ def main():
             del r
             torch.cuda.empty_cache()
     line["secondary"] = secondary
+
+    if args.copy_calibration:
+        nbytes = 256 << 20
+        src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        src.fill_(1)
+        for _ in range(3):
+            cf.copy_bytes(src, dst)
+        torch.cuda.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 20
+        start.record()
+        for _ in range(reps):
+            cf.copy_bytes(src, dst)
+        end.record()
+        torch.cuda.synchronize()
+        ms_copy = start.elapsed_time(end) / reps
+        line["copy_calibration"] = {"bytes_read": nbytes, "bytes_written": nbytes, "ms": ms_copy,
+                                    "GB/s (read+write)": round(2 * nbytes / (ms_copy * 1e-3) / 1e9, 1)}
+        del src, dst
 
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(work)

@@ -4,31 +4,41 @@
 // section 1 (Y[n,y,x,o] = sum over i,j,c of X[n,y+i,x+j,c] * F[i,j,c,o]).
 // Section 5 writes it as a product of the (N*Ho*Wo) x (K*K*Cin) patch matrix
 // with F reshaped to (K*K*Cin) x Cout; section 6 prices the copy that builds
-// the patch matrix. This kernel never builds it: input rows are staged once
-// in LDS and every patch fragment is read from there with a per-tap offset
-// (the 6-axis patch view of section 5 turned into LDS addressing).
+// the patch matrix. This kernel never builds it: a band's input rows are
+// staged once in LDS and every patch fragment is read from there with a
+// per-tap offset (the 6-axis patch view of section 5 turned into LDS
+// addressing).
 //
 // Work decomposition (one workgroup = 8 waves = 512 threads, 2 per SIMD):
-//  * A workgroup owns a band of R consecutive output rows of one image and a
-//    tile of 64 output channels.
-//  * The filter slice F[:, :, :, tile] is loaded once, transposed through LDS,
-//    and then held in registers (A operand of v_mfma_f32_16x16x32_bf16) for
-//    the whole band. Wave w keeps the 32-channel half (w & 1) of the tile:
+//  * A workgroup owns a band of R output rows of one image and a tile of 64
+//    output channels. It walks its R + KH - 1 input rows (at most NR) top to
+//    bottom, keeping the loads of the next four rows in flight in registers.
+//  * The filter slice F[:, :, :, tile] is transposed through LDS and then held
+//    in registers as the A operand of v_mfma_f32_16x16x32_bf16 for the whole
+//    band. Wave w keeps the 32-channel half (w & 1) of the tile:
 //    KH*KW*ceil(Cin/32) k-steps x 2 column blocks x 4 registers.
-//  * Input rows flow through an LDS ring of KH+1 rows. Row y+KH is written
-//    while output row y is computed; global loads for the next PF rows sit
-//    in registers, so HBM latency overlaps the matrix work.
+//  * Each input row is committed to LDS once, and every X fragment read
+//    from it feeds all KH output rows that use that input row (one
+//    accumulator set per output row in flight), so LDS traffic per output
+//    row is KW*CS fragment reads rather than KH*KW*CS.
 //  * Output row y is cut into 16-pixel blocks; wave pair (2g, 2g+1) takes
-//    blocks g, g+4. Per k-step a lane reads 8 channels of one pixel (16
+//    blocks g, g+4. Per fragment a lane reads 8 channels of one pixel (16
 //    bytes, B operand) and issues one MFMA per 16-channel column block of its
-//    half. The two waves sharing a SIMD hide each other's LDS latency.
+//    half into each output row in flight: KH*2 independent accumulation
+//    chains per wave.
 //  * The product is computed transposed (rows = output channels, columns =
-//    pixels), so each lane ends with 4 consecutive channels of one pixel and
-//    stores them with one vector write.
+//    pixels). Each row of results is parked in an LDS tile and leaves as
+//    16-byte chunks, so every store instruction writes whole cache lines.
 //
-// LDS pixel pitch is Cin_padded + 8 bf16 (16 bytes of padding): eight lanes
-// reading eight consecutive pixels hit eight distinct bank groups.
-// Channels beyond Cin (up to the multiple of 32) are zero in LDS.
+// LDS pixel pitch is Cin_padded + 16 bf16 (32 bytes of padding). Measured on
+// gfx950, 16-byte LDS reads whose 16 lanes step through consecutive pixels
+// run conflict-free only when the pitch is 32 modulo 64 bytes (96, 160, 288,
+// 544 B all reach ~190 B/clk per CU; pitches of 16, 48 or 0 modulo 64 lose
+// about 40%). Channels beyond Cin (up to the multiple of 32) are zero.
+//
+// All global accesses are raw buffer operations: out-of-range offsets are
+// dropped by the hardware (loads return zeros), which masks ragged edges
+// without branches around memory operations.
 #include <type_traits>
 
 #include "common.h"
@@ -39,17 +49,17 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int THREADS = 512;
 constexpr int COUT_TILE = 64;      // 4 column blocks of 16 output channels
 constexpr int NBW = 2;             // column blocks per wave (its half of the tile)
-constexpr int PF = 3;              // input rows in registers ahead of the ring
 constexpr int LDS_BYTES_MAX = 160 * 1024;
 constexpr uint32_t OOB = 0x80000000u;           // buffer offset beyond every range: access dropped
 constexpr int BUF_WORD3 = 0x00020000;           // raw buffer descriptor word 3 (gfx9 family)
-
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 struct RowArgs {
     const uint16_t *X;
@@ -60,8 +70,9 @@ struct RowArgs {
     int H, W, Cin, Cout, Ho, Wo;
     int R;              // output rows per band
     int bands_per_img;
-    int row_elems;      // LDS elements per ring row (W * pitch)
+    int row_elems;      // LDS elements per staged input row (W * pitch)
     int chunks_per_row; // 16-byte chunks per staged input row (W * Cin_padded / 8)
+    int otile_off;      // LDS byte offset of the output tiles
     uint32_t x_records; // bytes addressable from one image's base in X
     uint32_t y_records; // bytes addressable from one image's base in Y
 };
@@ -80,13 +91,13 @@ __device__ __forceinline__ uint32_t chunk_off(const RowArgs &a, int r, int q, in
 }
 
 template <int CINP>
-__device__ __forceinline__ void put_chunk(uint16_t *ring_row, int q, u32x4 v)
+__device__ __forceinline__ void put_chunk(uint16_t *lds_row, int q, u32x4 v)
 {
     constexpr int CG = CINP / 8;
-    constexpr int PITCH = CINP + 8;
+    constexpr int PITCH = CINP + 16;
     const int px = q / CG;
     const int cg = q - px * CG;
-    *reinterpret_cast<u32x4 *>(ring_row + px * PITCH + cg * 8) = v;
+    *reinterpret_cast<u32x4 *>(lds_row + px * PITCH + cg * 8) = v;
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
@@ -105,19 +116,29 @@ __device__ __forceinline__ void static_for(Fn &&fn)
     }
 }
 
-template <int KH, int KW, int CS, int BPW, int MAXC, bool OUT_BF16>
+template <int KH, int KW, int CS, int BPW, int MAXC, int NR, bool OUT_BF16>
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void dense_rows_mfma(RowArgs a)
 {
     constexpr int CINP = 32 * CS;
-    constexpr int PITCH = CINP + 8;
+    constexpr int PITCH = CINP + 16;
+    constexpr int FPITCH = COUT_TILE + 8;      // filter staging row: 64 outputs + 16 bytes
     constexpr int KSTEPS = KH * KW * CS;
-    constexpr int NSLOT = KH + 1;
     constexpr int ESZ = OUT_BF16 ? 2 : 4;
+    // Output tile: one row of results (64 pixels per block slot x 64
+    // channels), double buffered, padded to a pitch of 32 mod 64 bytes.
+    constexpr int OPITCH = COUT_TILE * ESZ + 32;
+    constexpr int OTILE_BYTES = 64 * BPW * OPITCH;
+    constexpr int OCH = COUT_TILE * ESZ / 16;                        // 16-byte chunks per pixel
+    constexpr int OSTORE = (64 * BPW * OCH + THREADS - 1) / THREADS;  // store instructions per row
 
+    // LDS: [filter staging, later the input rows] [output tiles]. The filter
+    // staging area is dead once the fragments are in registers; the input
+    // rows are committed into it afterwards (the host sizes it for both).
     extern __shared__ __align__(16) uint16_t smem[];
-    uint16_t *ring = smem;
-    uint16_t *ft = smem + NSLOT * a.row_elems;
+    uint16_t *ft = smem;
+    uint16_t *rows = smem;
+    uint8_t *otile = reinterpret_cast<uint8_t *>(smem) + a.otile_off;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -125,7 +146,11 @@ void dense_rows_mfma(RowArgs a)
     const int half = wave & 1;          // which 32 output channels of the tile
     const int pg = wave >> 1;           // pixel-block group 0..3
     const int o0 = blockIdx.y * COUT_TILE;
-    const int band = blockIdx.x;
+    // Workgroups are dealt to the 8 XCDs round robin by launch order. Map
+    // launch slot s to band (s % 8) * (grid/8) + s / 8 so that consecutive
+    // bands of one image run on one XCD and their shared halo rows meet in
+    // that XCD's L2. The map is a bijection when gridDim.x % 8 == 0.
+    const int band = (gridDim.x % 8 == 0) ? (int)((blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8) : (int)blockIdx.x;
     const int n = band / a.bands_per_img;
     const int y0 = (band - n * a.bands_per_img) * a.R;
     if (y0 >= a.Ho)
@@ -138,18 +163,10 @@ void dense_rows_mfma(RowArgs a)
     const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(
         static_cast<char *>(a.Y) + (int64_t)n * a.ys0 * ESZ, 0, (int)a.y_records, BUF_WORD3);
 
-    // 1. Input rows y0 .. y0+KH-1, the filter slice and the bias: issue every
-    //    global load first, then write LDS, so the latencies overlap.
-    u32x4 pro[KH][MAXC];
-#pragma unroll
-    for (int i = 0; i < KH; ++i)
-#pragma unroll
-        for (int k = 0; k < MAXC; ++k)
-            pro[i][k] = __builtin_amdgcn_raw_buffer_load_b128(xr, chunk_off<CINP>(a, y0 + i, tid + k * THREADS, rows_end), 0, 0);
-
-    // Filter: item it -> (c fastest, then 8-channel output group, then tap),
-    // so the 2-byte transposed LDS writes of a wave hit consecutive addresses.
-    // Padding channels and output channels past Cout load as zeros.
+    // 1. Filter slice and bias first. Item it -> (8-channel output group og
+    //    fastest, then input channel c, then tap): eight lanes cover one
+    //    128-byte row of F, so the loads are coalesced. Padding channels and
+    //    outputs past Cout load as zeros.
     constexpr int FITEMS = (KH * KW * CINP * 8 + THREADS - 1) / THREADS;
     const __amdgpu_buffer_rsrc_t fr = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t *>(a.F), 0, KH * KW * a.Cin * a.Cout * 2, BUF_WORD3);
@@ -157,9 +174,9 @@ void dense_rows_mfma(RowArgs a)
 #pragma unroll
     for (int t = 0; t < FITEMS; ++t) {
         const int it = tid + t * THREADS;
-        const int c = it % CINP;
-        const int og = (it / CINP) & 7;
-        const int tap = it / (CINP * 8);
+        const int og = it & 7;
+        const int c = (it >> 3) % CINP;
+        const int tap = (it >> 3) / CINP;
         const int o = o0 + og * 8;
         const bool ok = tap < KH * KW && c < a.Cin && o < a.Cout;
         fv[t] = __builtin_amdgcn_raw_buffer_load_b128(
@@ -173,128 +190,188 @@ void dense_rows_mfma(RowArgs a)
     for (int nb = 0; nb < NBW; ++nb)
         bq[nb] = __builtin_amdgcn_raw_buffer_load_b128(
             br, (uint32_t)((o0 + half * 32 + nb * 16 + (lane >> 4) * 4) * 4), 0, 0);
-    // Next PF-1 rows into the register queue.
-    u32x4 stage[PF][MAXC];
+
+    // 2. The first D input rows of the band; the loop below keeps loading D
+    //    rows ahead of use. The fence keeps the scheduler from hoisting these
+    //    above the filter loads (the counter is in order, so the filter wait
+    //    would then also wait for the rows).
+    __builtin_amdgcn_sched_barrier(0);
+    constexpr int D = NR < 4 ? NR : 4;
+    u32x4 xin[D][MAXC];
 #pragma unroll
-    for (int p = 0; p < PF - 1; ++p)
+    for (int i = 0; i < D; ++i)
 #pragma unroll
         for (int k = 0; k < MAXC; ++k)
-            stage[p][k] = __builtin_amdgcn_raw_buffer_load_b128(
-                xr, chunk_off<CINP>(a, y0 + KH + p, tid + k * THREADS, rows_end), 0, 0);
+            xin[i][k] = __builtin_amdgcn_raw_buffer_load_b128(
+                xr, chunk_off<CINP>(a, y0 + i, tid + k * THREADS, rows_end), 0, 0);
 
-#pragma unroll
-    for (int i = 0; i < KH; ++i)
-#pragma unroll
-        for (int k = 0; k < MAXC; ++k) {
-            const int q = tid + k * THREADS;
-            if (q < a.chunks_per_row)
-                put_chunk<CINP>(ring + i * a.row_elems, q, pro[i][k]);
-        }
+    // 3. Filter tile into LDS in its natural layout ft[tap][c][o], rows of
+    //    64 outputs padded to FPITCH elements: plain 16-byte writes.
 #pragma unroll
     for (int t = 0; t < FITEMS; ++t) {
         const int it = tid + t * THREADS;
-        const int c = it % CINP;
-        const int og = (it / CINP) & 7;
-        const int tap = it / (CINP * 8);
-        if (tap < KH * KW) {
-            const uint32_t w4[4] = {fv[t][0], fv[t][1], fv[t][2], fv[t][3]};
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                ft[(tap * COUT_TILE + og * 8 + e) * PITCH + c] = (uint16_t)(w4[e >> 1] >> ((e & 1) * 16));
-        }
+        const int og = it & 7;
+        const int c = (it >> 3) % CINP;
+        const int tap = (it >> 3) / CINP;
+        if (tap < KH * KW)
+            *reinterpret_cast<u32x4 *>(ft + (tap * CINP + c) * FPITCH + og * 8) = fv[t];
     }
     __syncthreads();
 
-    // 2. Filter fragments into registers: lane holds F^T[o = 32*half + 16nb + lane%16][8 channels].
+    // 4. Filter fragments into registers with the gfx950 transpose read
+    //    (ds_read_b64_tr_b16). Within each 16-lane group, output lane i gets
+    //    element i % 4 of the 8-byte chunk addressed by lane 4j + i/4, for
+    //    j = 0..3. Lane r of the group therefore addresses row r/4, columns
+    //    4*(r%4)..+3 of a 4-row block of ft, and receives F[c0+j][o0+i]:
+    //    four consecutive input channels of one output channel, which is the
+    //    A-operand layout (lane holds 8 consecutive k of row o = lane % 16).
+    //    Two reads give the 8 channels of the lane's k-group.
     bf16x8 wf[KSTEPS][NBW];
+    {
+        const int g = lane >> 4;           // k-group: channels 8g..8g+7 of a 32-channel step
+        const int r = lane & 15;
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-        const int tap = ks / CS;
-        const int cs = ks % CS;
+        for (int ks = 0; ks < KSTEPS; ++ks) {
+            const int tap = ks / CS;
+            const int cs = ks % CS;
 #pragma unroll
-        for (int nb = 0; nb < NBW; ++nb)
-            wf[ks][nb] = *reinterpret_cast<const bf16x8 *>(
-                ft + (tap * COUT_TILE + half * 32 + nb * 16 + (lane & 15)) * PITCH + cs * 32 + (lane >> 4) * 8);
+            for (int nb = 0; nb < NBW; ++nb) {
+                i16x4 part[2];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int c = cs * 32 + g * 8 + h * 4 + (r >> 2);
+                    const int o = half * 32 + nb * 16 + 4 * (r & 3);
+                    part[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) i16x4 *)(ft + (tap * CINP + c) * FPITCH + o));
+                }
+                const i16x8 both = {part[0][0], part[0][1], part[0][2], part[0][3],
+                                    part[1][0], part[1][1], part[1][2], part[1][3]};
+                wf[ks][nb] = __builtin_bit_cast(bf16x8, both);
+            }
+        }
     }
+    __syncthreads();      // the staging area becomes the input-row area
 
-    // 3. One output row: prefetch, matrix work, store, commit, barrier. Every
-    //    global memory operation here is unconditional (invalid lanes use
-    //    out-of-range buffer offsets), so the compiler can count outstanding
-    //    loads exactly and keep PF rows in flight.
-    auto row_step = [&](const int y, auto U) {
-        constexpr int u = decltype(U)::value;
+    // 5. Input row 0 into LDS.
 #pragma unroll
-        for (int k = 0; k < MAXC; ++k)
-            stage[(u + PF - 1) % PF][k] = __builtin_amdgcn_raw_buffer_load_b128(
-                xr, chunk_off<CINP>(a, y + KH + PF - 1, tid + k * THREADS, rows_end), 0, 0);
+    for (int k = 0; k < MAXC; ++k) {
+        const int q = tid + k * THREADS;
+        if (q < a.chunks_per_row)
+            put_chunk<CINP>(rows, q, xin[0][k]);
+    }
+    __syncthreads();
 
-        const uint16_t *rowp[KH];
+    // A finished output row leaves as 16-byte chunks from its LDS tile:
+    // consecutive lanes write consecutive bytes of consecutive pixels, so
+    // every store instruction writes whole cache lines. Rows past the band
+    // and lanes past the row use out-of-range offsets (dropped).
+    auto store_row = [&](const int t) __attribute__((always_inline)) {
+        const uint8_t *obuf = otile + (t & 1) * OTILE_BYTES;
+        const int yo = y0 + t;
 #pragma unroll
-        for (int i = 0; i < KH; ++i)
-            rowp[i] = ring + ((y - y0 + i) % NSLOT) * a.row_elems;
+        for (int k = 0; k < OSTORE; ++k) {
+            const int q = tid + k * THREADS;
+            const int px = q / OCH;               // pixel
+            const int cc = q - px * OCH;          // 16-byte chunk within the pixel's tile row
+            const int ch = o0 + cc * (16 / ESZ);
+            const bool ok = px < a.Wo && ch < a.Cout && yo < y1;
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(obuf + (px < 64 * BPW ? px : 0) * OPITCH + cc * 16);
+            const uint32_t off = ok ? (uint32_t)(((int64_t)yo * a.ys1 + (int64_t)px * a.ys2 + ch) * ESZ) : OOB;
+            __builtin_amdgcn_raw_buffer_store_b128(v, yr, off, 0, 0);
+        }
+    };
 
+    // 6. Slide down the band one input row at a time. Input row r feeds
+    //    output rows t = r - i for filter rows i = 0..KH-1, so each X fragment
+    //    read from LDS serves up to KH output rows: KW*CS fragments per input
+    //    row instead of KH*KW*CS per output row. Output row t accumulates in
+    //    slot t % KH during steps t .. t+KH-1 (taps in ascending i, then j,
+    //    then channel step); at step t+KH-1 it is complete, goes to output
+    //    tile t & 1, and leaves at step t+KH after the barrier.
+    //    The loop is fully unrolled (NR steps, all indices static) and every
+    //    global operation in it is unconditional, so the waits the compiler
+    //    places for prefetched rows never include the stores.
+    f32x4 acc[KH][BPW][NBW];
+#pragma unroll
+    for (int s2 = 0; s2 < KH; ++s2)
+#pragma unroll
+        for (int qb = 0; qb < BPW; ++qb)
+#pragma unroll
+            for (int nb = 0; nb < NBW; ++nb)
+                acc[s2][qb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    static_for<0, NR>([&](auto RR) {
+        constexpr int r = decltype(RR)::value;
+        if constexpr (r >= KH)
+            store_row(r - KH);
+        if constexpr (r + D < NR) {
+#pragma unroll
+            for (int k = 0; k < MAXC; ++k)
+                xin[(r + D) % D][k] = __builtin_amdgcn_raw_buffer_load_b128(
+                    xr, chunk_off<CINP>(a, y0 + r + D, tid + k * THREADS, rows_end), 0, 0);
+        }
+        const uint16_t *rowp = rows + r * a.row_elems;
 #pragma unroll
         for (int qb = 0; qb < BPW; ++qb) {
             const int x = (pg + 4 * qb) * 16 + (lane & 15);
             const int xl = min(x, a.Wo - 1);
-            f32x4 acc[NBW];
+            bf16x8 xb[KW * CS];
 #pragma unroll
-            for (int nb = 0; nb < NBW; ++nb)
-                acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < KSTEPS; ++ks) {
-                const int tap = ks / CS;
-                const int i = tap / KW;
-                const int j = tap % KW;
-                const int cs = ks % CS;
-                const bf16x8 xb = *reinterpret_cast<const bf16x8 *>(
-                    rowp[i] + (xl + j) * PITCH + cs * 32 + (lane >> 4) * 8);
-#pragma unroll
-                for (int nb = 0; nb < NBW; ++nb)
-                    acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[ks][nb], xb, acc[nb], 0, 0, 0);
+            for (int jc = 0; jc < KW * CS; ++jc) {
+                const int j = jc / CS;
+                const int cs = jc % CS;
+                xb[jc] = *reinterpret_cast<const bf16x8 *>(rowp + (xl + j) * PITCH + cs * 32 + (lane >> 4) * 8);
             }
-            // Lane holds channels o0+32*half+16nb+4*(lane/16)+{0..3} of pixel x.
 #pragma unroll
-            for (int nb = 0; nb < NBW; ++nb) {
-                const int ch0 = o0 + half * 32 + nb * 16 + (lane >> 4) * 4;
-                const bool ok = x < a.Wo && ch0 < a.Cout;
-                const uint32_t off = ok ? (uint32_t)(((int64_t)y * a.ys1 + (int64_t)x * a.ys2 + ch0) * ESZ) : OOB;
-                const float v0 = acc[nb][0] + __uint_as_float(bq[nb][0]);
-                const float v1 = acc[nb][1] + __uint_as_float(bq[nb][1]);
-                const float v2 = acc[nb][2] + __uint_as_float(bq[nb][2]);
-                const float v3 = acc[nb][3] + __uint_as_float(bq[nb][3]);
-                if constexpr (OUT_BF16) {
-                    const u32x2 w = {pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
-                    __builtin_amdgcn_raw_buffer_store_b64(w, yr, off, 0, 0);
-                } else {
-                    const u32x4 w = {__float_as_uint(v0), __float_as_uint(v1), __float_as_uint(v2), __float_as_uint(v3)};
-                    __builtin_amdgcn_raw_buffer_store_b128(w, yr, off, 0, 0);
+            for (int i = 0; i < KH; ++i) {
+                const int t = r - i;                     // output row fed by filter row i
+                if (t >= 0 && t <= NR - KH && y0 + t < y1) {
+#pragma unroll
+                    for (int jc = 0; jc < KW * CS; ++jc) {
+                        const int ks = i * KW * CS + jc;
+#pragma unroll
+                        for (int nb = 0; nb < NBW; ++nb)
+                            acc[(t + KH) % KH][qb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                wf[ks][nb], xb[jc], acc[(t + KH) % KH][qb][nb], 0, 0, 0);
+                    }
+                }
+            }
+            if constexpr (r >= KH - 1) {
+                // Output row t = r - KH + 1 is complete: lane holds channels
+                // 32*half+16nb+4*(lane/16)+{0..3} of pixel x.
+                constexpr int t = r - KH + 1;
+                uint8_t *orow = otile + (t & 1) * OTILE_BYTES + x * OPITCH;
+#pragma unroll
+                for (int nb = 0; nb < NBW; ++nb) {
+                    const int cl = half * 32 + nb * 16 + (lane >> 4) * 4;
+                    const f32x4 v = acc[t % KH][qb][nb];
+                    const float v0 = v[0] + __uint_as_float(bq[nb][0]);
+                    const float v1 = v[1] + __uint_as_float(bq[nb][1]);
+                    const float v2 = v[2] + __uint_as_float(bq[nb][2]);
+                    const float v3 = v[3] + __uint_as_float(bq[nb][3]);
+                    if constexpr (OUT_BF16) {
+                        *reinterpret_cast<u32x2 *>(orow + cl * 2) = u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+                    } else {
+                        *reinterpret_cast<u32x4 *>(orow + cl * 4) =
+                            u32x4{__float_as_uint(v0), __float_as_uint(v1), __float_as_uint(v2), __float_as_uint(v3)};
+                    }
+                    acc[t % KH][qb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
                 }
             }
         }
-
-        // Commit input row y+KH (loaded PF-1 rows ago) into the ring slot of
-        // row y-1, which no wave reads any more.
-        const int r = y + KH;
-        if (r < rows_end) {
-            uint16_t *dst = ring + ((r - y0) % NSLOT) * a.row_elems;
+        if constexpr (r + 1 < NR) {
+            // Input row r+1 into LDS for the next step (rows past the band
+            // are zeros and never feed a stored output).
 #pragma unroll
             for (int k = 0; k < MAXC; ++k) {
                 const int q = tid + k * THREADS;
                 if (q < a.chunks_per_row)
-                    put_chunk<CINP>(dst, q, stage[u][k]);
+                    put_chunk<CINP>(rows + (r + 1) * a.row_elems, q, xin[(r + 1) % D][k]);
             }
         }
         __syncthreads();
-    };
-
-    int y = y0;
-    for (; y + PF <= y1; y += PF)
-        static_for<0, PF>([&](auto U) { row_step(y + decltype(U)::value, U); });
-    static_for<0, PF - 1>([&](auto U) {
-        if (y + decltype(U)::value < y1)
-            row_step(y + decltype(U)::value, U);
     });
+    store_row(NR - KH);
 }
 
 // --- host side -------------------------------------------------------------
@@ -319,16 +396,12 @@ bool taps_instantiated(int KH, int KW, int CS)
     return false;
 }
 
-size_t lds_bytes(const DenseProblem &p, int CS)
-{
-    const int cinp = 32 * CS;
-    const size_t pitch = (size_t)cinp + 8;
-    return ((size_t)(p.KH + 1) * p.W * pitch + (size_t)p.KH * p.KW * COUT_TILE * pitch) * 2;
-}
+// Input rows a workgroup keeps in registers, by 16-byte chunks per thread.
+constexpr int rows_in_regs(int MAXC) { return MAXC == 1 ? 9 : MAXC == 2 ? 4 : 2; }
 
 struct Plan {
-    int CS, BPW, MAXC;
-    size_t lds;
+    int CS, BPW, MAXC, NR, R;
+    size_t otile_off, lds;
 };
 
 // Bytes addressable from one image's base: the extent of the last element.
@@ -341,50 +414,70 @@ bool plan_rows(const DenseProblem &p, Plan *plan)
 {
     if (p.xdt != CONV_BF16 || p.Cin % 8 != 0 || p.Cout % 8 != 0)
         return false;
-    if ((uintptr_t)p.F % 16 != 0 || (int64_t)p.KH * p.KW * p.Cin * p.Cout * 2 >= (int64_t(1) << 31))
-        return false;
     if ((uintptr_t)p.X % 16 != 0 || p.xs[0] % 8 != 0 || p.xs[1] % 8 != 0 || p.xs[2] % 8 != 0)
         return false;
+    if ((uintptr_t)p.F % 16 != 0 || (int64_t)p.KH * p.KW * p.Cin * p.Cout * 2 >= (int64_t(1) << 31))
+        return false;
+    // Output rows leave in 16-byte chunks of 8 (bf16) or 4 (fp32) channels.
     const int yesz = p.ydt == CONV_BF16 ? 2 : 4;
-    if ((uintptr_t)p.Y % (4 * yesz) != 0 || p.ys[0] % 4 != 0 || p.ys[1] % 4 != 0 || p.ys[2] % 4 != 0)
+    const int yvec = 16 / yesz;
+    if ((uintptr_t)p.Y % 16 != 0 || p.ys[0] % yvec != 0 || p.ys[1] % yvec != 0 || p.ys[2] % yvec != 0)
         return false;
     // Buffer offsets are 32-bit: one image of X and of Y must stay below 2 GB.
     if (image_extent(p.xs, p.H, p.W, p.Cin, 2) >= (int64_t(1) << 31) ||
         image_extent(p.ys, p.Ho, p.Wo, p.Cout, yesz) >= (int64_t(1) << 31))
         return false;
-    const int CS = cin_steps(p.Cin);
-    if (CS == 0 || !taps_instantiated(p.KH, p.KW, CS))
+    Plan pl;
+    pl.CS = cin_steps(p.Cin);
+    if (pl.CS == 0 || !taps_instantiated(p.KH, p.KW, pl.CS))
         return false;
     const int blocks = (p.Wo + 15) / 16;
-    const int BPW = (blocks + 3) / 4;
-    if (BPW > 2)
+    pl.BPW = (blocks + 3) / 4;
+    if (pl.BPW > 2)
         return false;
-    const int64_t chunks = (int64_t)p.W * 32 * CS / 8;
-    const int MAXC = chunks <= THREADS ? 1 : chunks <= 2 * THREADS ? 2 : chunks <= 4 * THREADS ? 4 : 0;
-    if (MAXC == 0)
+    const int64_t chunks = (int64_t)p.W * 32 * pl.CS / 8;
+    pl.MAXC = chunks <= THREADS ? 1 : chunks <= 2 * THREADS ? 2 : chunks <= 4 * THREADS ? 4 : 0;
+    if (pl.MAXC == 0)
         return false;
-    const size_t lds = lds_bytes(p, CS);
-    if (lds > (size_t)LDS_BYTES_MAX)
+    pl.NR = rows_in_regs(pl.MAXC);
+    const int rmax = pl.NR - p.KH + 1;             // output rows a band can hold
+    if (rmax < 1)
         return false;
-    plan->CS = CS;
-    plan->BPW = BPW;
-    plan->MAXC = MAXC;
-    plan->lds = lds;
+    // Bands: aim for about one workgroup per compute unit (256) in total.
+    const int tiles = (p.Cout + COUT_TILE - 1) / COUT_TILE;
+    int want = (int)((256 + (int64_t)p.N * tiles - 1) / ((int64_t)p.N * tiles));
+    want = want < 1 ? 1 : want > p.Ho ? p.Ho : want;
+    const int R = (p.Ho + want - 1) / want;
+    pl.R = R < rmax ? R : rmax;
+    // LDS: [max(filter staging, input rows)] [two output tiles].
+    const size_t pitch = (size_t)32 * pl.CS + 16;
+    const size_t filt = (size_t)p.KH * p.KW * 32 * pl.CS * (COUT_TILE + 8) * 2;
+    const size_t rows = (size_t)pl.NR * p.W * pitch * 2;
+    pl.otile_off = filt > rows ? filt : rows;
+    pl.lds = pl.otile_off + 2 * (size_t)64 * pl.BPW * (COUT_TILE * yesz + 32);
+    if (pl.lds > (size_t)LDS_BYTES_MAX)
+        return false;
+    *plan = pl;
     return true;
 }
 
 template <int KH, int KW, int CS, int BPW, int MAXC, bool OB>
 hipError_t launch_inst(const RowArgs &a, dim3 grid, size_t lds, hipStream_t s)
 {
-    auto kern = dense_rows_mfma<KH, KW, CS, BPW, MAXC, OB>;
-    // Allow the full LDS once per instantiation (first launch, before any
-    // graph capture a caller may start later).
-    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                                       hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES_MAX);
-    if (attr != hipSuccess)
-        return attr;
-    hipLaunchKernelGGL(kern, grid, dim3(THREADS), lds, s, a);
-    return hipGetLastError();
+    constexpr int NR = rows_in_regs(MAXC);
+    if constexpr (NR - KH + 1 < 1) {
+        return hipErrorNotSupported;
+    } else {
+        auto kern = dense_rows_mfma<KH, KW, CS, BPW, MAXC, NR, OB>;
+        // Allow the full LDS once per instantiation (first launch, before any
+        // graph capture a caller may start later).
+        static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                                           hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES_MAX);
+        if (attr != hipSuccess)
+            return attr;
+        hipLaunchKernelGGL(kern, grid, dim3(THREADS), lds, s, a);
+        return hipGetLastError();
+    }
 }
 
 template <int KH, int KW, int CS, int BPW>
@@ -435,20 +528,14 @@ hipError_t launch_dense_tiled(const DenseProblem &p, hipStream_t s)
     a.Cout = p.Cout;
     a.Ho = p.Ho;
     a.Wo = p.Wo;
-    a.row_elems = p.W * (32 * plan.CS + 8);
+    a.row_elems = p.W * (32 * plan.CS + 16);
     a.chunks_per_row = p.W * 32 * plan.CS / 8;
+    a.otile_off = (int)plan.otile_off;
     a.x_records = (uint32_t)image_extent(p.xs, p.H, p.W, p.Cin, 2);
     a.y_records = (uint32_t)image_extent(p.ys, p.Ho, p.Wo, p.Cout, p.ydt == CONV_BF16 ? 2 : 4);
-
-    // Bands: aim for one workgroup per compute unit (256) in total.
-    const int tiles = (p.Cout + COUT_TILE - 1) / COUT_TILE;
-    int want = (int)((256 + (int64_t)p.N * tiles - 1) / ((int64_t)p.N * tiles));
-    if (want < 1)
-        want = 1;
-    if (want > p.Ho)
-        want = p.Ho;
-    a.R = (p.Ho + want - 1) / want;
+    a.R = plan.R;
     a.bands_per_img = (p.Ho + a.R - 1) / a.R;
+    const int tiles = (p.Cout + COUT_TILE - 1) / COUT_TILE;
     const dim3 grid((unsigned)(p.N * a.bands_per_img), (unsigned)tiles);
     const bool ob = p.ydt == CONV_BF16;
 
