@@ -1,0 +1,379 @@
+// Depthwise convolution staged through LDS: the bandwidth-bound kernel.
+//
+// "Depthwise convolution" (onemodel docs), sections "What each output is"
+// and "How the kernel is organised": output plane q = (n, oc) reads input
+// plane q / multiplier; the sum starts at +0 and takes the taps row by row;
+// a tap outside the input multiplies a real +0; exact mode rounds each
+// product and then each sum, fast mode fuses them; the bias is one more
+// rounded addition and exact mode rewrites a NaN result to 0x7FC00000. The
+// same page asks for identical bits on every code path, so this kernel must
+// reproduce the direct kernel (and the oracle) exactly: it differs only in
+// how the input reaches the arithmetic, never in the arithmetic or its order.
+//
+// Organisation (one workgroup = 256 threads):
+//  * A tile is PPW consecutive output planes (small planes) or a band of RB
+//    output rows of one plane (large planes). Its input is one contiguous
+//    range of X (NCHW planes are contiguous, and so are consecutive rows and
+//    consecutive planes). The workgroup copies that range, widened to 16-byte
+//    chunks plus a few elements of slack on each side, into LDS with 16-byte
+//    buffer loads, all issued before the first wait so the whole tile is in
+//    flight at once. Chunks outside X load as zeros.
+//  * Stride 2: the copy splits elements by the parity of their index into
+//    two phase planes (even half, odd half). Input columns 2*ox + kx of
+//    neighbouring lanes then sit at neighbouring LDS words, as they do at
+//    stride 1, so tap reads stay free of bank conflicts. (Row lengths are
+//    even, so index parity is column parity.)
+//  * A thread owns one output column of RT consecutive output rows (the
+//    narrow-row idea: each input value read from LDS serves up to KH of the
+//    thread's outputs). Neighbouring lanes own neighbouring columns.
+//  * Taps that fall in the padding read whatever neighbour sits in LDS and
+//    replace it with +0 before the multiply: the arithmetic sees exactly the
+//    zero the definition puts there.
+//  * The weights of the thread's plane stay in registers; the thread stores
+//    its RT outputs directly (neighbouring lanes write neighbouring words).
+#include <algorithm>
+
+#include "common.h"
+#include "internal.h"
+
+namespace convfwd {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int THREADS = 256;
+constexpr int BATCH = 8;             // 16-byte loads in flight per thread per round
+constexpr int SLACK = 12;            // LDS elements before/after the tile range (>= max pad, multiple of 4)
+constexpr int MAX_PAD = 8;
+constexpr uint32_t OOB = 0x80000000u;
+constexpr int BUF_WORD3 = 0x00020000;
+constexpr int LDS_LIMIT = 64 * 1024;
+
+// n / d for 0 <= n < 2^31 by multiply-high (division by an invariant integer).
+struct FastDiv {
+    uint32_t m, s;
+};
+
+FastDiv make_fastdiv(uint32_t d)
+{
+    uint32_t s = 0;
+    while ((1ull << s) < d)
+        ++s;
+    const uint64_t m = ((1ull << 32) * ((1ull << s) - d)) / d + 1;
+    return FastDiv{(uint32_t)m, s};
+}
+
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) { return (__umulhi(n, f.m) + n) >> f.s; }
+
+struct TileArgs {
+    const float *X;
+    const float *w;
+    const float *bias;
+    float *Y;
+    int64_t XE;        // elements of X
+    int64_t HW;        // elements per input plane
+    int H, W, Cout, Ho, Wo, ph, pw;
+    int planes;        // N * Cout output planes
+    int PPW;           // output planes per tile
+    int bands;         // tiles per plane (1 when PPW > 1)
+    int RB;            // output rows per band
+    int TPP;           // threads per plane: (row groups) * Wo
+    int half;          // LDS elements per phase plane (stride 2)
+    FastDiv div_bands, div_tpp, div_wo, div_mult;
+};
+
+template <int KH, int KW, int S, int RT, int EXACT>
+__global__ __launch_bounds__(THREADS) void dw_tiled_kernel(TileArgs a)
+{
+#pragma clang fp contract(off)
+    extern __shared__ __align__(16) float lds[];
+    const int tid = threadIdx.x;
+
+    // Tile: output planes [q0, qend), output rows [oy_lo, oy_hi).
+    const uint32_t tile = fdiv(blockIdx.x, a.div_bands);
+    const int band = (int)(blockIdx.x - tile * (uint32_t)a.bands);
+    const int q0 = (int)tile * a.PPW;
+    const int qend = min(q0 + a.PPW, a.planes);
+    const int oy_lo = band * a.RB;
+    const int oy_hi = min(a.Ho, oy_lo + a.RB);
+    // Input rows any output of the tile reads, clipped to the plane.
+    const int iy_lo = max(0, oy_lo * S - a.ph);
+    const int iy_hi = min(a.H, (oy_hi - 1) * S - a.ph + KH);
+    const int ip0 = (int)fdiv((uint32_t)q0, a.div_mult);
+    const int ip1 = (int)fdiv((uint32_t)(qend - 1), a.div_mult);
+    const int64_t e0 = (int64_t)ip0 * a.HW + (int64_t)iy_lo * a.W;
+    const int64_t e1 = (int64_t)ip1 * a.HW + (int64_t)iy_hi * a.W;
+    const int64_t a0 = (e0 & ~(int64_t)3) - SLACK;                 // X index of LDS element 0
+    const int nchunks = (int)((((e1 + 3) & ~(int64_t)3) + SLACK - a0) >> 2);
+
+    // The thread's task (decided now so the weight loads overlap the copy).
+    const int p = (int)fdiv((uint32_t)tid, a.div_tpp);
+    const int rem = tid - p * a.TPP;
+    const int g = (int)fdiv((uint32_t)rem, a.div_wo);
+    const int ox = rem - g * a.Wo;
+    const int q = q0 + p;
+    const int oy0 = oy_lo + g * RT;
+    const bool active = p < a.PPW && q < qend && oy0 < oy_hi;
+    const int qc = active ? q : q0;
+    const int ip = (int)fdiv((uint32_t)qc, a.div_mult);
+    const int occ = qc % a.Cout;
+    float wv[KH * KW];
+#pragma unroll
+    for (int k = 0; k < KH * KW; ++k)
+        wv[k] = a.w[(int64_t)occ * (KH * KW) + k];
+
+    // Copy the tile range into LDS, BATCH chunks per thread per round: all
+    // loads of a round are issued before the first write waits for them.
+    const int64_t abase = a0 > 0 ? a0 : 0;
+    const int64_t avail = (a.XE - abase) * 4;
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float *>(a.X + abase), 0, (int)(avail < 0x7FFFFFF0 ? avail : 0x7FFFFFF0), BUF_WORD3);
+    for (int base = 0; base < nchunks; base += THREADS * BATCH) {
+        f32x4 v[BATCH];
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) {
+            const int k = base + tid + u * THREADS;
+            const int64_t e = a0 + 4 * (int64_t)k;
+            const bool ok = k < nchunks && e >= 0 && e < a.XE;
+            v[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                 xr, ok ? (uint32_t)((e - abase) * 4) : OOB, 0, 0));
+        }
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) {
+            const int k = base + tid + u * THREADS;
+            if (k < nchunks) {
+                if constexpr (S == 1) {
+                    *reinterpret_cast<f32x4 *>(lds + 4 * k) = v[u];
+                } else {
+                    *reinterpret_cast<f32x2 *>(lds + 2 * k) = f32x2{v[u][0], v[u][2]};
+                    *reinterpret_cast<f32x2 *>(lds + a.half + 2 * k) = f32x2{v[u][1], v[u][3]};
+                }
+            }
+        }
+    }
+    __syncthreads();
+    if (!active)
+        return;
+
+    // Column validity of each tap (the same for every row).
+    const int ix0 = ox * S - a.pw;
+    bool cok[KW];
+#pragma unroll
+    for (int kx = 0; kx < KW; ++kx)
+        cok[kx] = (unsigned)(ix0 + kx) < (unsigned)a.W;
+
+    // Input row iy of plane ip sits at LDS element (ip*HW + iy*W - a0) (stride
+    // 1). Rows outside the plane are read from a clamped row and zeroed.
+    const int plane_rel = (int)((int64_t)ip * a.HW - a0);
+    float acc[RT];
+#pragma unroll
+    for (int t = 0; t < RT; ++t)
+        acc[t] = +0.0f;
+
+    constexpr int NIR = (RT - 1) * S + KH;     // input rows the thread's outputs read
+#pragma unroll
+    for (int ir = 0; ir < NIR; ++ir) {
+        const int iy = oy0 * S - a.ph + ir;
+        const bool rok = (unsigned)iy < (unsigned)a.H;
+        const int iyc = min(max(iy, iy_lo), iy_hi - 1);
+        const int rb = plane_rel + iyc * a.W + ix0;   // LDS element of tap kx = 0 (stride 1)
+        float xv[KW];
+        if constexpr (S == 1) {
+#pragma unroll
+            for (int kx = 0; kx < KW; ++kx)
+                xv[kx] = lds[rb + kx];
+        } else {
+            // Element e lives at (e & 1) * half + (e >> 1); rb >= 0 here.
+            const int b0 = (rb & 1) * a.half + (rb >> 1);
+            const int b1 = ((rb + 1) & 1) * a.half + ((rb + 1) >> 1);
+#pragma unroll
+            for (int kx = 0; kx < KW; ++kx)
+                xv[kx] = (kx & 1) ? lds[b1 + (kx >> 1)] : lds[b0 + (kx >> 1)];
+        }
+#pragma unroll
+        for (int kx = 0; kx < KW; ++kx)
+            xv[kx] = (rok && cok[kx]) ? xv[kx] : +0.0f;
+        // This input row is filter row ky = ir - t*S of output row t.
+#pragma unroll
+        for (int t = 0; t < RT; ++t) {
+            const int ky = ir - t * S;
+            if (ky >= 0 && ky < KH) {
+#pragma unroll
+                for (int kx = 0; kx < KW; ++kx) {
+                    if constexpr (EXACT) {
+                        const float prod = wv[ky * KW + kx] * xv[kx];
+                        acc[t] = acc[t] + prod;
+                    } else {
+                        acc[t] = __builtin_fmaf(wv[ky * KW + kx], xv[kx], acc[t]);
+                    }
+                }
+            }
+        }
+    }
+
+    const float bv = a.bias ? a.bias[occ] : 0.0f;
+    float *yp = a.Y + (int64_t)q * a.Ho * a.Wo + ox;
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+        const int oy = oy0 + t;
+        if (oy < oy_hi) {
+            float r = acc[t];
+            if (a.bias)
+                r = r + bv;
+            if (EXACT && __builtin_isnan(r))
+                r = __uint_as_float(0x7FC00000u);
+            yp[(int64_t)oy * a.Wo] = r;
+        }
+    }
+}
+
+// --- host side -------------------------------------------------------------
+
+struct TilePlan {
+    int RT, PPW, bands, RB, TPP;
+    int64_t lds_elems;
+    double util;
+};
+
+// Tile shape for rows-per-thread RT: whole planes when a plane's outputs fit
+// one workgroup, else bands of rows of one plane. A constant of the shape.
+TilePlan plan_for(const DwProblem &p, int RT)
+{
+    TilePlan t{};
+    t.RT = RT;
+    const int S = p.sh;
+    const int groups_full = (p.Ho + RT - 1) / RT;
+    if ((int64_t)groups_full * p.Wo <= THREADS) {
+        t.TPP = groups_full * p.Wo;
+        t.PPW = THREADS / t.TPP;
+        t.bands = 1;
+        t.RB = groups_full * RT;
+    } else {
+        const int gr = THREADS / p.Wo;
+        t.TPP = gr * p.Wo;
+        t.PPW = 1;
+        t.RB = gr * RT;
+        t.bands = (p.Ho + t.RB - 1) / t.RB;
+    }
+    const int64_t HW = (int64_t)p.H * p.W;
+    auto lds_for = [&](int ppw) {
+        // q0/mult .. (q0+ppw-1)/mult: at most ceil((ppw-1)/mult) plane steps.
+        const int64_t plane_steps = (ppw - 1 + p.mult - 1) / p.mult;
+        const int64_t rows = std::min<int64_t>(p.H, (int64_t)(t.RB - 1) * S + p.KH);
+        const int64_t elems = plane_steps * HW + rows * p.W + 8 + 2 * SLACK;
+        return ((elems + 3) / 4) * 4;
+    };
+    while (t.PPW > 1 && lds_for(t.PPW) * 4 > LDS_LIMIT)
+        --t.PPW;
+    t.lds_elems = lds_for(t.PPW);
+    const int64_t planes = (int64_t)p.N * p.C * p.mult;
+    const int64_t tiles = (planes + t.PPW - 1) / t.PPW * t.bands;
+    const double slots = (double)tiles * THREADS * RT;
+    t.util = (double)planes * p.Ho * p.Wo / slots;
+    return t;
+}
+
+bool plan(const DwProblem &p, TilePlan &out)
+{
+    if (!((p.KH == 3 && p.KW == 3) || (p.KH == 5 && p.KW == 5)))
+        return false;
+    if (p.sh != p.sw || (p.sh != 1 && p.sh != 2) || p.dh != 1 || p.dw != 1)
+        return false;
+    if (p.ph > MAX_PAD || p.pw > MAX_PAD || p.ph >= p.KH || p.pw >= p.KW || p.Wo > THREADS)
+        return false;       // every output window must overlap the input
+    if (p.sh == 2 && (p.W % 2) != 0)
+        return false;       // phase planes need even rows
+    const int64_t XE = (int64_t)p.N * p.C * p.H * p.W;
+    const int64_t planes = (int64_t)p.N * p.C * p.mult;
+    if (XE % 4 != 0 || (reinterpret_cast<uintptr_t>(p.X) & 15) != 0)
+        return false;       // 16-byte chunks must tile X exactly
+    if (planes >= (1ll << 31) - THREADS || planes * p.Ho * p.Wo >= (1ll << 40))
+        return false;
+    bool have = false;
+    for (int RT : {4, 7}) {
+        TilePlan t = plan_for(p, RT);
+        if (t.lds_elems * 4 > LDS_LIMIT)
+            continue;
+        if (!have || t.util > out.util + 1e-9 || (t.util > out.util - 1e-9 && RT > out.RT)) {
+            out = t;
+            have = true;
+        }
+    }
+    if (have) {
+        const int64_t tiles = (planes + out.PPW - 1) / out.PPW * out.bands;
+        if (tiles >= (1ll << 31))
+            return false;
+    }
+    return have;
+}
+
+template <int KH, int KW, int S, int RT>
+hipError_t launch_rt(const TileArgs &a, unsigned grid, size_t lds, bool exact, hipStream_t s)
+{
+    if (exact)
+        hipLaunchKernelGGL((dw_tiled_kernel<KH, KW, S, RT, 1>), dim3(grid), dim3(THREADS), lds, s, a);
+    else
+        hipLaunchKernelGGL((dw_tiled_kernel<KH, KW, S, RT, 0>), dim3(grid), dim3(THREADS), lds, s, a);
+    return hipGetLastError();
+}
+
+template <int KH, int KW, int S>
+hipError_t launch_s(const TileArgs &a, int RT, unsigned grid, size_t lds, bool exact, hipStream_t s)
+{
+    return RT == 4 ? launch_rt<KH, KW, S, 4>(a, grid, lds, exact, s) : launch_rt<KH, KW, S, 7>(a, grid, lds, exact, s);
+}
+
+template <int KH, int KW>
+hipError_t launch_k(const TileArgs &a, int S, int RT, unsigned grid, size_t lds, bool exact, hipStream_t s)
+{
+    return S == 1 ? launch_s<KH, KW, 1>(a, RT, grid, lds, exact, s) : launch_s<KH, KW, 2>(a, RT, grid, lds, exact, s);
+}
+
+}  // namespace
+
+bool dw_tiled_supports(const DwProblem &p)
+{
+    TilePlan t;
+    return plan(p, t);
+}
+
+hipError_t launch_dw_tiled(const DwProblem &p, hipStream_t s)
+{
+    TilePlan t;
+    if (!plan(p, t))
+        return hipErrorNotSupported;
+    TileArgs a;
+    a.X = p.X;
+    a.w = p.w;
+    a.bias = p.bias;
+    a.Y = p.Y;
+    a.XE = (int64_t)p.N * p.C * p.H * p.W;
+    a.HW = (int64_t)p.H * p.W;
+    a.H = p.H;
+    a.W = p.W;
+    a.Cout = p.C * p.mult;
+    a.Ho = p.Ho;
+    a.Wo = p.Wo;
+    a.ph = p.ph;
+    a.pw = p.pw;
+    a.planes = p.N * p.C * p.mult;
+    a.PPW = t.PPW;
+    a.bands = t.bands;
+    a.RB = t.RB;
+    a.TPP = t.TPP;
+    // Phase planes: half of the LDS range each (the range is a multiple of 4).
+    a.half = (int)(t.lds_elems / 2);
+    a.div_bands = make_fastdiv((uint32_t)t.bands);
+    a.div_tpp = make_fastdiv((uint32_t)t.TPP);
+    a.div_wo = make_fastdiv((uint32_t)p.Wo);
+    a.div_mult = make_fastdiv((uint32_t)p.mult);
+    const int64_t tiles = ((int64_t)a.planes + t.PPW - 1) / t.PPW * t.bands;
+    const size_t lds = (size_t)t.lds_elems * 4;
+    const bool exact = p.mode == CONV_DW_EXACT;
+    if (p.KH == 3)
+        return launch_k<3, 3>(a, p.sh, t.RT, (unsigned)tiles, lds, exact, s);
+    return launch_k<5, 5>(a, p.sh, t.RT, (unsigned)tiles, lds, exact, s);
+}
+
+}  // namespace convfwd

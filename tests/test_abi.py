@@ -147,8 +147,15 @@ def test_auto_variant_queries(lib):
     assert lib.conv2d_nhwc_auto_variant(None, XA, 0, 8, 8, 3, 3, 3, 4, 0, 0) == -1
     assert lib.conv2d_nhwc_auto_variant(None, XA, 2, 8, 8, 3, 3, 3, 4, 0, 0) in (cf.VARIANT_DIRECT, cf.VARIANT_TILED)
     assert lib.conv_depthwise_auto_variant(1, 1, 3, 3, 1, 5, 5, 1, 1, 0, 0, 1, 1) == -1
-    v = lib.conv_depthwise_auto_variant(8, 72, 56, 56, 1, 5, 5, 2, 2, 2, 2, 1, 1)
-    assert v in (cf.VARIANT_DIRECT, cf.VARIANT_TILED)
+    # Every measured depthwise workload runs on the LDS-tiled kernel.
+    import workloads as wl
+    for l in (wl.DW_5X5S2_EXACT, *wl.DW_SWEEP):
+        v = lib.conv_depthwise_auto_variant(l.N, l.C, l.H, l.W, l.mult, l.KH, l.KW, l.stride, l.stride,
+                                            l.pad, l.pad, l.dil, l.dil)
+        assert v == cf.VARIANT_TILED, l.name
+    # Shapes the tiled kernel does not take fall back to the direct kernel.
+    assert lib.conv_depthwise_auto_variant(2, 4, 11, 11, 3, 3, 3, 3, 3, 0, 0, 1, 1) == cf.VARIANT_DIRECT
+    assert lib.conv_depthwise_auto_variant(1, 2, 19, 23, 1, 3, 3, 1, 1, 2, 2, 2, 2) == cf.VARIANT_DIRECT
 
 
 def test_binding_rejects_cpu_tensors(lib):

@@ -100,6 +100,37 @@ def test_gpu_dw_odd_shapes_bitwise(case, mode):
     check(X, w, bias=b, stride=s, padding=p, dilation=d, mode=mode)
 
 
+# Shapes the LDS-tiled kernel takes, chosen to hit its tile boundaries:
+# planes that do not divide into whole tiles, ragged row bands, multipliers
+# whose output planes straddle tiles, both strides, both kernel sizes, odd
+# padding, bias. Each runs on every variant (auto, direct, tiled) and must
+# give the oracle's bits.
+TILED = [  # N, C, H, W, mult, K, stride, pad, bias
+    (2, 4, 12, 12, 3, 3, 1, 1, True),
+    (3, 5, 14, 14, 2, 5, 2, 2, False),
+    (1, 3, 8, 8, 1, 5, 1, 0, True),
+    (1, 2, 100, 60, 1, 3, 1, 1, False),       # 4 bands, last one ragged
+    (1, 3, 58, 46, 1, 5, 2, 2, True),         # stride 2, ragged band
+    (2, 3, 30, 30, 1, 5, 1, 1, False),        # pad 1 with a 5x5 window
+    (1, 6, 9, 12, 4, 3, 2, 0, True),          # multiplier 4, stride 2, no pad
+    (4, 37, 7, 8, 1, 5, 1, 2, False),         # tiles of 36 planes, 148 planes
+    (1, 1, 250, 250, 1, 3, 1, 1, False),      # widest rows the kernel takes
+    (1, 2, 226, 226, 1, 3, 2, 1, True),       # stride 2 onto 113 columns
+]
+
+
+@pytest.mark.parametrize("case", TILED)
+@pytest.mark.parametrize("mode", ["exact", "fast"])
+def test_gpu_dw_tiled_shapes_bitwise(case, mode):
+    N, C, H, W, m, K, s, p, has_bias = case
+    assert cf.depthwise_variant_for((N, C, H, W), (C * m, K, K), s, p) == cf.VARIANT_TILED
+    seed = 6000 + TILED.index(case)
+    X = wl.random_tensor((N, C, H, W), seed)
+    w = wl.random_tensor((C * m, K, K), seed + 1)
+    b = wl.random_tensor((C * m,), seed + 2) if has_bias else None
+    check(X, w, bias=b, stride=s, padding=p, mode=mode)
+
+
 # --- the pages' examples and special values ------------------------------------
 
 def test_gpu_dw_worked_examples():
