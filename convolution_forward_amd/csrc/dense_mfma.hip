@@ -12,7 +12,9 @@
 // Work decomposition (one workgroup = 8 waves = 512 threads, 2 per SIMD):
 //  * A workgroup owns a band of R output rows of one image and a tile of 64
 //    output channels. It walks its R + KH - 1 input rows (at most NR) top to
-//    bottom, keeping the loads of the next four rows in flight in registers.
+//    bottom, keeping the loads of the next two to four rows in flight in
+//    registers. A 1x1 filter makes pixels independent: pixel-contiguous
+//    inputs are regrouped into rows of 64 pixels first.
 //  * The filter slice F[:, :, :, tile] is transposed through LDS and then held
 //    in registers as the A operand of v_mfma_f32_16x16x32_bf16 for the whole
 //    band. Wave w keeps the 32-channel half (w & 1) of the tile:
@@ -70,6 +72,8 @@ struct RowArgs {
     int H, W, Cin, Cout, Ho, Wo;
     int R;              // output rows per band
     int bands_per_img;
+    int bands;          // N * bands_per_img (the grid may hold more: those exit)
+    int tiles;          // 64-channel output tiles
     int row_elems;      // LDS elements per staged input row (W * pitch)
     int chunks_per_row; // 16-byte chunks per staged input row (W * Cin_padded / 8)
     int otile_off;      // LDS byte offset of the output tiles
@@ -132,9 +136,10 @@ void dense_rows_mfma(RowArgs a)
     constexpr int OCH = COUT_TILE * ESZ / 16;                        // 16-byte chunks per pixel
     constexpr int OSTORE = (64 * BPW * OCH + THREADS - 1) / THREADS;  // store instructions per row
 
-    // LDS: [filter staging, later the input rows] [output tiles]. The filter
-    // staging area is dead once the fragments are in registers; the input
-    // rows are committed into it afterwards (the host sizes it for both).
+    // LDS: [filter staging, later two input-row buffers] [output tiles]. The
+    // filter staging area is dead once the fragments are in registers; input
+    // row r is then committed into buffer r & 1 (the host sizes the area for
+    // both uses).
     extern __shared__ __align__(16) uint16_t smem[];
     uint16_t *ft = smem;
     uint16_t *rows = smem;
@@ -145,12 +150,17 @@ void dense_rows_mfma(RowArgs a)
     const int wave = tid >> 6;
     const int half = wave & 1;          // which 32 output channels of the tile
     const int pg = wave >> 1;           // pixel-block group 0..3
-    const int o0 = blockIdx.y * COUT_TILE;
-    // Workgroups are dealt to the 8 XCDs round robin by launch order. Map
-    // launch slot s to band (s % 8) * (grid/8) + s / 8 so that consecutive
-    // bands of one image run on one XCD and their shared halo rows meet in
-    // that XCD's L2. The map is a bijection when gridDim.x % 8 == 0.
-    const int band = (gridDim.x % 8 == 0) ? (int)((blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8) : (int)blockIdx.x;
+    // Workgroups are dealt to the 8 XCDs round robin by launch order (slot s
+    // runs on XCD s % 8). The grid holds a multiple of 8 bands times the
+    // output tiles; slot s takes band (s % 8) * (bands/8) + (s/8) / tiles and
+    // tile (s/8) % tiles. All tiles of a band and consecutive bands of one
+    // image then run on one XCD, so the input rows they share (the whole band
+    // across tiles, the halo rows across bands) meet in that XCD's L2.
+    const int slot_in_xcd = (int)(blockIdx.x >> 3);
+    const int band = (int)(blockIdx.x & 7) * (int)(gridDim.x >> 3) / a.tiles + slot_in_xcd / a.tiles;
+    const int o0 = (slot_in_xcd % a.tiles) * COUT_TILE;
+    if (band >= a.bands)
+        return;
     const int n = band / a.bands_per_img;
     const int y0 = (band - n * a.bands_per_img) * a.R;
     if (y0 >= a.Ho)
@@ -196,7 +206,8 @@ void dense_rows_mfma(RowArgs a)
     //    above the filter loads (the counter is in order, so the filter wait
     //    would then also wait for the rows).
     __builtin_amdgcn_sched_barrier(0);
-    constexpr int D = NR < 4 ? NR : 4;
+    constexpr int DW = MAXC == 1 ? 4 : 2;    // rows of loads in flight (register budget)
+    constexpr int D = NR < DW ? NR : DW;
     u32x4 xin[D][MAXC];
 #pragma unroll
     for (int i = 0; i < D; ++i)
@@ -310,7 +321,7 @@ void dense_rows_mfma(RowArgs a)
                 xin[(r + D) % D][k] = __builtin_amdgcn_raw_buffer_load_b128(
                     xr, chunk_off<CINP>(a, y0 + r + D, tid + k * THREADS, rows_end), 0, 0);
         }
-        const uint16_t *rowp = rows + r * a.row_elems;
+        const uint16_t *rowp = rows + (r & 1) * a.row_elems;
 #pragma unroll
         for (int qb = 0; qb < BPW; ++qb) {
             const int x = (pg + 4 * qb) * 16 + (lane & 15);
@@ -360,13 +371,15 @@ void dense_rows_mfma(RowArgs a)
             }
         }
         if constexpr (r + 1 < NR) {
-            // Input row r+1 into LDS for the next step (rows past the band
-            // are zeros and never feed a stored output).
+            // Input row r+1 into the other buffer for the next step (its
+            // previous row was last read before the barrier that ended the
+            // previous step; rows past the band are zeros and never feed a
+            // stored output).
 #pragma unroll
             for (int k = 0; k < MAXC; ++k) {
                 const int q = tid + k * THREADS;
                 if (q < a.chunks_per_row)
-                    put_chunk<CINP>(rows + (r + 1) * a.row_elems, q, xin[(r + 1) % D][k]);
+                    put_chunk<CINP>(rows + ((r + 1) & 1) * a.row_elems, q, xin[(r + 1) % D][k]);
             }
         }
         __syncthreads();
@@ -396,8 +409,10 @@ bool taps_instantiated(int KH, int KW, int CS)
     return false;
 }
 
-// Input rows a workgroup keeps in registers, by 16-byte chunks per thread.
-constexpr int rows_in_regs(int MAXC) { return MAXC == 1 ? 9 : MAXC == 2 ? 4 : 2; }
+// Input rows a band walks (the unrolled step count). Only the loads of the
+// next few rows are held in registers, so this is bounded by code size, not
+// by registers or LDS.
+constexpr int rows_in_regs(int MAXC) { return MAXC == 1 ? 9 : MAXC == 2 ? 9 : 13; }
 
 struct Plan {
     int CS, BPW, MAXC, NR, R;
@@ -449,10 +464,10 @@ bool plan_rows(const DenseProblem &p, Plan *plan)
     want = want < 1 ? 1 : want > p.Ho ? p.Ho : want;
     const int R = (p.Ho + want - 1) / want;
     pl.R = R < rmax ? R : rmax;
-    // LDS: [max(filter staging, input rows)] [two output tiles].
+    // LDS: [max(filter staging, two input rows)] [two output tiles].
     const size_t pitch = (size_t)32 * pl.CS + 16;
     const size_t filt = (size_t)p.KH * p.KW * 32 * pl.CS * (COUT_TILE + 8) * 2;
-    const size_t rows = (size_t)pl.NR * p.W * pitch * 2;
+    const size_t rows = (size_t)2 * p.W * pitch * 2;
     pl.otile_off = filt > rows ? filt : rows;
     pl.lds = pl.otile_off + 2 * (size_t)64 * pl.BPW * (COUT_TILE * yesz + 32);
     if (pl.lds > (size_t)LDS_BYTES_MAX)
@@ -500,14 +515,63 @@ hipError_t launch_cs(const RowArgs &a, dim3 grid, const Plan &plan, bool ob, hip
 
 }  // namespace
 
+// A 1x1 filter makes every pixel independent: when the pixels of X and Y
+// sit at one pixel stride (within each image, or across the whole batch),
+// regroup them into rows of 64 (or another width that divides the pixel
+// count) so no 16-pixel block of a row is left partly empty.
+DenseProblem regroup_pointwise(const DenseProblem &p)
+{
+    if (p.KH != 1 || p.KW != 1)
+        return p;
+    if (p.xs[1] != (int64_t)p.W * p.xs[2] || p.ys[1] != (int64_t)p.Wo * p.ys[2])
+        return p;
+    const bool batch = p.xs[0] == (int64_t)p.H * p.xs[1] && p.ys[0] == (int64_t)p.Ho * p.ys[1];
+    const int64_t pixels = batch ? (int64_t)p.N * p.H * p.W : (int64_t)p.H * p.W;
+    int best = 0;
+    double best_score = 0;
+    for (int w = 16; w <= 128; ++w) {
+        if (pixels % w != 0)
+            continue;
+        const double fill = (double)w / (16.0 * ((w + 15) / 16));
+        const double score = fill * (w >= 64 ? 1.0 : (double)w / 64.0) + (w == 64 ? 1e-3 : 0.0);
+        if (score > best_score) {
+            best_score = score;
+            best = w;
+        }
+    }
+    if (best == 0 || pixels / best >= (int64_t(1) << 31))
+        return p;
+    DenseProblem q = p;
+    q.N = batch ? 1 : p.N;
+    q.W = q.Wo = best;
+    q.H = q.Ho = (int)(pixels / best);
+    q.xs[1] = (int64_t)best * p.xs[2];
+    q.ys[1] = (int64_t)best * p.ys[2];
+    if (batch) {
+        q.xs[0] = q.H * q.xs[1];
+        q.ys[0] = q.Ho * q.ys[1];
+    }
+    // Keep the regrouped shape only if the kernel takes it and the original
+    // one is worse off (a row of the original already fills its blocks).
+    Plan a, b;
+    const bool ok_q = plan_rows(q, &a);
+    const bool ok_p = plan_rows(p, &b);
+    if (!ok_q)
+        return p;
+    if (ok_p && p.Wo % 16 == 0 && p.Wo >= 64)
+        return p;
+    return q;
+}
+
 bool dense_tiled_supports(const DenseProblem &p)
 {
     Plan plan;
-    return plan_rows(p, &plan);
+    return plan_rows(regroup_pointwise(p), &plan);
 }
 
-hipError_t launch_dense_tiled(const DenseProblem &p, hipStream_t s)
+hipError_t launch_dense_tiled(const DenseProblem &p0, hipStream_t s)
 {
+    const DenseProblem p = regroup_pointwise(p0);
     Plan plan;
     if (!plan_rows(p, &plan))
         return hipErrorNotSupported;
@@ -535,8 +599,14 @@ hipError_t launch_dense_tiled(const DenseProblem &p, hipStream_t s)
     a.y_records = (uint32_t)image_extent(p.ys, p.Ho, p.Wo, p.Cout, p.ydt == CONV_BF16 ? 2 : 4);
     a.R = plan.R;
     a.bands_per_img = (p.Ho + a.R - 1) / a.R;
-    const int tiles = (p.Cout + COUT_TILE - 1) / COUT_TILE;
-    const dim3 grid((unsigned)(p.N * a.bands_per_img), (unsigned)tiles);
+    a.bands = p.N * a.bands_per_img;
+    a.tiles = (p.Cout + COUT_TILE - 1) / COUT_TILE;
+    // One slot per (band, tile), bands padded to a multiple of 8 (the
+    // padding slots exit at once) for the XCD-aware slot map.
+    const int64_t slots = (int64_t)((a.bands + 7) / 8 * 8) * a.tiles;
+    if (slots >= (int64_t(1) << 31))
+        return hipErrorNotSupported;
+    const dim3 grid((unsigned)slots);
     const bool ob = p.ydt == CONV_BF16;
 
     switch (p.KH * 100 + p.KW * 10) {

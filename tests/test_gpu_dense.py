@@ -187,6 +187,47 @@ def test_gpu_dense_write_coverage_and_determinism(variant):
     assert torch.equal(Y1.view(torch.int16), Y2.view(torch.int16))
 
 
+# --- 1x1 filters: the pixel regrouping and the layouts that prevent it --------
+
+POINTWISE = [  # name, X base shape, X view slices, Cout
+    ("batch_contiguous", (4, 10, 13, 64), None, 80),          # 520 pixels, regrouped into rows of 104
+    ("prime_pixels", (1, 1, 127, 32), None, 24),               # 127 pixels: no regrouping
+    ("image_contiguous", (3, 9, 16, 48), "batch", 40),         # batch stride padded
+    ("cropped", (2, 12, 20, 32), "crop", 64),                  # rows not at one pixel stride
+    ("channel_slice", (2, 7, 9, 96), "chan", 72),              # pixel stride 96, 64 channels used
+]
+
+
+@pytest.mark.parametrize("case", POINTWISE, ids=lambda c: c[0])
+def test_gpu_dense_pointwise_layouts(case):
+    name, shape, view, O = case
+    seed = 7000 + POINTWISE.index(case)
+    base = wl.random_tensor(shape, seed).to(torch.bfloat16).to(DEV)
+    if view == "batch":
+        big = torch.zeros((shape[0], shape[1] + 1, shape[2], shape[3]), dtype=torch.bfloat16, device=DEV)
+        big[:, :shape[1]] = base
+        X = big[:, :shape[1]]
+    elif view == "crop":
+        X = base[:, 1:-1, 2:-1]
+    elif view == "chan":
+        X = base[..., 16:80]
+    else:
+        X = base
+    C = X.shape[-1]
+    F = (wl.random_tensor((1, 1, C, O), seed + 1) * (1.0 / C ** 0.5)).to(torch.bfloat16)
+    b = wl.random_tensor((O,), seed + 2)
+    ref = oracle.conv2d_nhwc(X.cpu(), F, bias=b)
+    for variant in [cf.VARIANT_AUTO] + VARIANTS:
+        if not supported(X, F.to(DEV), variant, torch.float32):
+            continue
+        out = torch.full(tuple(X.shape[:3]) + (O + 8,), float("nan"), dtype=torch.float32, device=DEV)
+        Y = run(X, F, bias=b, variant=variant, out=out[..., :O], out_dtype=torch.float32)
+        assert rms_rel_err(Y, ref) <= 1e-3, variant
+        assert torch.isnan(out[..., O:]).all()
+        Yb = run(X, F, bias=b, variant=variant)
+        assert rms_rel_err(Yb, ref) <= BF16_RMS_REL and bf16_ulp_distance(Yb, ref) <= 1
+
+
 # --- the full-size workloads, in the launch configuration the benchmark uses ---
 
 def sample_indices(shape, n, seed):
