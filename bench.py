@@ -35,6 +35,13 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2516.6   # dense bf16 MFMA (256 CU x 4096 FLOP/clk x 2.4 GHz)
 F32_MFMA_PEAK_TFLOPS = 157.3     # dense fp32 MFMA
 COLD_BYTES = 1 << 30             # rotate at least this much distinct memory in cold mode
+# Measured HBM bytes per launch of the headline kernel: FETCH_SIZE and
+# WRITE_SIZE per dispatch from two rocprofv3 --pmc runs, each scaled by what
+# the same counter reads for the plain copy kernel of known size. The file
+# records the hash of the kernel source it was taken on; once the source
+# changes the figure no longer describes the kernel and is reported as null.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "dense_rows_mfma_dense3x3_bf16_traffic.txt")
+HEADLINE_SOURCE = os.path.join(ROOT, "convolution_forward_amd", "csrc", "dense_mfma.hip")
 
 
 def parse():
@@ -179,6 +186,26 @@ def measure(runner, steps, warmup, trials, reps_cap=None):
     return ms, n
 
 
+def measured_traffic():
+    """HBM bytes per launch from the committed counter summary, or None when
+    it is missing or was taken on a different kernel source."""
+    import hashlib
+    try:
+        fields = {}
+        with open(TRAFFIC_FILE) as f:
+            for ln in f:
+                if ":" in ln and not ln.startswith("#"):
+                    k, v = ln.split(":", 1)
+                    fields[k.strip()] = v.strip()
+        with open(HEADLINE_SOURCE, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+        if fields.get("kernel_source_sha256") != sha:
+            return None
+        return float(fields["traffic_bytes_per_dispatch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(work):
     """The oracle, untuned, on a bounded sample of the headline workload: the
     first images of the batch, sized to about 10-20 s of CPU work."""
@@ -246,7 +273,7 @@ def main():
                    "out_dtype": "bf16", "cache_mode": args.mode,
                    "buffer_sets": None, "kernel_variant": {1: "direct", 2: "mfma_implicit_gemm"}.get(variant)},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                      "algorithmic_bytes": set_bytes, "kernel_ms": ms,
                      "mfma_tflops": round(tflops, 2), "mfma_peak": BF16_MFMA_PEAK_TFLOPS,
                      "mfma_frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4)},
