@@ -1,7 +1,7 @@
 // Depthwise convolution staged through LDS: the bandwidth-bound kernel.
 //
 // "Depthwise convolution" (onemodel docs), sections "What each output is"
-// and "How the kernel is organised": output plane q = (n, oc) reads input
+// and "Layout of the work": output plane q = (n, oc) reads input
 // plane q / multiplier; the sum starts at +0 and takes the taps row by row;
 // a tap outside the input multiplies a real +0; exact mode rounds each
 // product and then each sum, fast mode fuses them; the bias is one more
