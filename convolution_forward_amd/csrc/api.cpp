@@ -136,6 +136,17 @@ conv_status validate_dense(const void *X, const int64_t *x_strides, const void *
     return CONV_OK;
 }
 
+// The tiled (matrix-core) variant: one kernel family per operand type.
+bool dense_tiled_supports(const DenseProblem &p)
+{
+    return p.xdt == CONV_BF16 ? dense_mfma_bf16_supports(p) : dense_mfma_f32_supports(p);
+}
+
+hipError_t launch_dense_tiled(const DenseProblem &p, hipStream_t s)
+{
+    return p.xdt == CONV_BF16 ? launch_dense_mfma_bf16(p, s) : launch_dense_mfma_f32(p, s);
+}
+
 int dense_auto(const DenseProblem &p) { return dense_tiled_supports(p) ? CONV_VARIANT_TILED : CONV_VARIANT_DIRECT; }
 
 // Shape and mode checks (no pointer checks); fills p except pointers.

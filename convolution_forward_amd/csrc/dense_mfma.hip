@@ -425,6 +425,14 @@ int64_t image_extent(const int64_t *s, int rows, int cols, int ch, int esz)
     return ((int64_t)(rows - 1) * s[1] + (int64_t)(cols - 1) * s[2] + ch) * esz;
 }
 
+// Loads per thread for one input row, at most, for rows that fit the
+// kernel (64 * BPW output pixels plus the halo).
+constexpr int max_chunks(int KW, int CS, int BPW) { return ((64 * BPW + KW - 1) * 4 * CS + THREADS - 1) / THREADS; }
+
+// Four chunks per thread are instantiated only for 1x1 filters: with a
+// larger window the row registers no longer fit beside the filter.
+constexpr bool wide_rows_ok(int KH) { return KH == 1; }
+
 bool plan_rows(const DenseProblem &p, Plan *plan)
 {
     if (p.xdt != CONV_BF16 || p.Cin % 8 != 0 || p.Cout % 8 != 0)
@@ -452,7 +460,7 @@ bool plan_rows(const DenseProblem &p, Plan *plan)
         return false;
     const int64_t chunks = (int64_t)p.W * 32 * pl.CS / 8;
     pl.MAXC = chunks <= THREADS ? 1 : chunks <= 2 * THREADS ? 2 : chunks <= 4 * THREADS ? 4 : 0;
-    if (pl.MAXC == 0)
+    if (pl.MAXC == 0 || (pl.MAXC == 4 && !wide_rows_ok(p.KH)))
         return false;
     pl.NR = rows_in_regs(pl.MAXC);
     const int rmax = pl.NR - p.KH + 1;             // output rows a band can hold
@@ -498,11 +506,18 @@ hipError_t launch_inst(const RowArgs &a, dim3 grid, size_t lds, hipStream_t s)
 template <int KH, int KW, int CS, int BPW>
 hipError_t launch_bpw(const RowArgs &a, dim3 grid, size_t lds, int MAXC, bool ob, hipStream_t s)
 {
-    switch (MAXC) {
-    case 1: return ob ? launch_inst<KH, KW, CS, BPW, 1, true>(a, grid, lds, s) : launch_inst<KH, KW, CS, BPW, 1, false>(a, grid, lds, s);
-    case 2: return ob ? launch_inst<KH, KW, CS, BPW, 2, true>(a, grid, lds, s) : launch_inst<KH, KW, CS, BPW, 2, false>(a, grid, lds, s);
-    default: return ob ? launch_inst<KH, KW, CS, BPW, 4, true>(a, grid, lds, s) : launch_inst<KH, KW, CS, BPW, 4, false>(a, grid, lds, s);
+    constexpr int CMAX = max_chunks(KW, CS, BPW);
+    if (MAXC == 1)
+        return ob ? launch_inst<KH, KW, CS, BPW, 1, true>(a, grid, lds, s) : launch_inst<KH, KW, CS, BPW, 1, false>(a, grid, lds, s);
+    if constexpr (CMAX >= 2) {
+        if (MAXC == 2)
+            return ob ? launch_inst<KH, KW, CS, BPW, 2, true>(a, grid, lds, s) : launch_inst<KH, KW, CS, BPW, 2, false>(a, grid, lds, s);
     }
+    if constexpr (CMAX >= 3 && wide_rows_ok(KH)) {
+        if (MAXC == 4)
+            return ob ? launch_inst<KH, KW, CS, BPW, 4, true>(a, grid, lds, s) : launch_inst<KH, KW, CS, BPW, 4, false>(a, grid, lds, s);
+    }
+    return hipErrorNotSupported;
 }
 
 template <int KH, int KW, int CS>
@@ -563,13 +578,13 @@ DenseProblem regroup_pointwise(const DenseProblem &p)
     return q;
 }
 
-bool dense_tiled_supports(const DenseProblem &p)
+bool dense_mfma_bf16_supports(const DenseProblem &p)
 {
     Plan plan;
     return plan_rows(regroup_pointwise(p), &plan);
 }
 
-hipError_t launch_dense_tiled(const DenseProblem &p0, hipStream_t s)
+hipError_t launch_dense_mfma_bf16(const DenseProblem &p0, hipStream_t s)
 {
     const DenseProblem p = regroup_pointwise(p0);
     Plan plan;

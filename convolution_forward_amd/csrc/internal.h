@@ -33,8 +33,10 @@ struct DwProblem {
 
 // Dense kernels.
 hipError_t launch_dense_direct(const DenseProblem &p, hipStream_t s);
-bool dense_tiled_supports(const DenseProblem &p);
-hipError_t launch_dense_tiled(const DenseProblem &p, hipStream_t s);
+bool dense_mfma_bf16_supports(const DenseProblem &p);
+hipError_t launch_dense_mfma_bf16(const DenseProblem &p, hipStream_t s);
+bool dense_mfma_f32_supports(const DenseProblem &p);
+hipError_t launch_dense_mfma_f32(const DenseProblem &p, hipStream_t s);
 
 // Depthwise kernels.
 hipError_t launch_dw_direct(const DwProblem &p, hipStream_t s);

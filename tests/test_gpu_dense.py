@@ -187,6 +187,35 @@ def test_gpu_dense_write_coverage_and_determinism(variant):
     assert torch.equal(Y1.view(torch.int16), Y2.view(torch.int16))
 
 
+# --- fp32 operands on the matrix-core kernel ------------------------------------
+
+F32_MFMA = [  # N, H, W, Cin, K, Cout
+    (2, 9, 66, 16, 3, 20),        # 64-pixel rows (two blocks per wave), partial channel tile
+    (1, 5, 34, 64, 3, 64),
+    (3, 6, 50, 32, 3, 72),        # two channel tiles, the second nearly empty
+    (2, 7, 11, 256, 1, 136),      # 1x1 regrouped, three channel tiles
+    (1, 3, 64, 48, 1, 8),
+]
+
+
+@pytest.mark.parametrize("shape", F32_MFMA)
+def test_gpu_dense_f32_matrix_cores(shape):
+    N, H, W, C, K, O = shape
+    seed = 8000 + F32_MFMA.index(shape)
+    X = wl.random_tensor((N, H, W, C), seed)
+    F = wl.random_tensor((K, K, C, O), seed + 1) * (1.0 / (K * K * C) ** 0.5)
+    b = wl.random_tensor((O,), seed + 2)
+    assert cf.dense_variant_for(X.to(DEV), F.to(DEV)) == cf.VARIANT_TILED
+    ref = oracle.conv2d_nhwc(X, F, bias=b)
+    Ho, Wo = H - K + 1, W - K + 1
+    big = torch.full((N, Ho, Wo, O + 8), float("nan"), dtype=torch.float32, device=DEV)
+    Y = run(X, F, bias=b, out=big[..., 4:O + 4], variant=cf.VARIANT_TILED)
+    assert max_rel_err(Y, ref) <= F32_MAX_REL
+    assert torch.isnan(big[..., :4]).all() and torch.isnan(big[..., O + 4:]).all()
+    Yd = run(X, F, bias=b, variant=cf.VARIANT_DIRECT)
+    assert max_rel_err(Yd, ref) <= F32_MAX_REL
+
+
 # --- 1x1 filters: the pixel regrouping and the layouts that prevent it --------
 
 POINTWISE = [  # name, X base shape, X view slices, Cout
