@@ -120,13 +120,105 @@ __device__ __forceinline__ void static_for(Fn &&fn)
     }
 }
 
+// Filter slice F[:, :, :, o0:o0+64] of a workgroup, in three steps shared
+// by both kernels: issue the loads, write the slice to LDS in its natural
+// layout ft[tap][c][o] (rows of 64 outputs padded to 72 elements), then read
+// the A fragments back with the gfx950 transpose read.
+//
+// Load item it -> (8-channel output group og fastest, then input channel c,
+// then tap): eight lanes cover one 128-byte row of F, so the loads are
+// coalesced. Padding channels and outputs past Cout load as zeros.
+template <int KH, int KW, int CS>
+struct FilterSlice {
+    static constexpr int CINP = 32 * CS;
+    static constexpr int FPITCH = COUT_TILE + 8;
+    static constexpr int KSTEPS = KH * KW * CS;
+    static constexpr int ITEMS = (KH * KW * CINP * 8 + THREADS - 1) / THREADS;
+    static constexpr size_t LDS_BYTES = (size_t)KH * KW * CINP * FPITCH * 2;
+
+    u32x4 fv[ITEMS];
+
+    __device__ __forceinline__ void issue(const RowArgs &a, int o0, int tid)
+    {
+        const __amdgpu_buffer_rsrc_t fr = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t *>(a.F), 0, KH * KW * a.Cin * a.Cout * 2, BUF_WORD3);
+#pragma unroll
+        for (int t = 0; t < ITEMS; ++t) {
+            const int it = tid + t * THREADS;
+            const int og = it & 7;
+            const int c = (it >> 3) % CINP;
+            const int tap = (it >> 3) / CINP;
+            const int o = o0 + og * 8;
+            const bool ok = tap < KH * KW && c < a.Cin && o < a.Cout;
+            fv[t] = __builtin_amdgcn_raw_buffer_load_b128(
+                fr, ok ? (uint32_t)((((int64_t)tap * a.Cin + c) * a.Cout + o) * 2) : OOB, 0, 0);
+        }
+    }
+
+    __device__ __forceinline__ void commit(uint16_t *ft, int tid) const
+    {
+#pragma unroll
+        for (int t = 0; t < ITEMS; ++t) {
+            const int it = tid + t * THREADS;
+            const int og = it & 7;
+            const int c = (it >> 3) % CINP;
+            const int tap = (it >> 3) / CINP;
+            if (tap < KH * KW)
+                *reinterpret_cast<u32x4 *>(ft + (tap * CINP + c) * FPITCH + og * 8) = fv[t];
+        }
+    }
+
+    // Within each 16-lane group of ds_read_b64_tr_b16, output lane i gets
+    // element i % 4 of the 8-byte chunk addressed by lane 4j + i/4, for
+    // j = 0..3. Lane r of the group therefore addresses row r/4, columns
+    // 4*(r%4)..+3 of a 4-row block of ft, and receives F[c0+j][o0+i]: four
+    // consecutive input channels of one output channel, which is the
+    // A-operand layout (lane holds 8 consecutive k of row o = lane % 16).
+    // Two reads give the 8 channels of the lane's k-group.
+    static __device__ __forceinline__ void fragments(const uint16_t *ft, int lane, int half, bf16x8 (&wf)[KSTEPS][NBW])
+    {
+        const int g = lane >> 4;           // k-group: channels 8g..8g+7 of a 32-channel step
+        const int r = lane & 15;
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks) {
+            const int tap = ks / CS;
+            const int cs = ks % CS;
+#pragma unroll
+            for (int nb = 0; nb < NBW; ++nb) {
+                i16x4 part[2];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int c = cs * 32 + g * 8 + h * 4 + (r >> 2);
+                    const int o = half * 32 + nb * 16 + 4 * (r & 3);
+                    part[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) i16x4 *)(ft + (tap * CINP + c) * FPITCH + o));
+                }
+                const i16x8 both = {part[0][0], part[0][1], part[0][2], part[0][3],
+                                    part[1][0], part[1][1], part[1][2], part[1][3]};
+                wf[ks][nb] = __builtin_bit_cast(bf16x8, both);
+            }
+        }
+    }
+};
+
+// Bias of the 4 output channels of each column block a lane's results
+// belong to (zeros without bias).
+__device__ __forceinline__ void bias_issue(const RowArgs &a, int o0, int half, int lane, u32x4 (&bq)[NBW])
+{
+    const __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc(
+        a.bias ? (void *)a.bias : (void *)a.F, 0, a.bias ? a.Cout * 4 : 0, BUF_WORD3);
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb)
+        bq[nb] = __builtin_amdgcn_raw_buffer_load_b128(
+            br, (uint32_t)((o0 + half * 32 + nb * 16 + (lane >> 4) * 4) * 4), 0, 0);
+}
+
 template <int KH, int KW, int CS, int BPW, int MAXC, int NR, bool OUT_BF16>
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void dense_rows_mfma(RowArgs a)
 {
     constexpr int CINP = 32 * CS;
     constexpr int PITCH = CINP + 16;
-    constexpr int FPITCH = COUT_TILE + 8;      // filter staging row: 64 outputs + 16 bytes
     constexpr int KSTEPS = KH * KW * CS;
     constexpr int ESZ = OUT_BF16 ? 2 : 4;
     // Output tile: one row of results (64 pixels per block slot x 64
@@ -173,33 +265,11 @@ void dense_rows_mfma(RowArgs a)
     const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(
         static_cast<char *>(a.Y) + (int64_t)n * a.ys0 * ESZ, 0, (int)a.y_records, BUF_WORD3);
 
-    // 1. Filter slice and bias first. Item it -> (8-channel output group og
-    //    fastest, then input channel c, then tap): eight lanes cover one
-    //    128-byte row of F, so the loads are coalesced. Padding channels and
-    //    outputs past Cout load as zeros.
-    constexpr int FITEMS = (KH * KW * CINP * 8 + THREADS - 1) / THREADS;
-    const __amdgpu_buffer_rsrc_t fr = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t *>(a.F), 0, KH * KW * a.Cin * a.Cout * 2, BUF_WORD3);
-    u32x4 fv[FITEMS];
-#pragma unroll
-    for (int t = 0; t < FITEMS; ++t) {
-        const int it = tid + t * THREADS;
-        const int og = it & 7;
-        const int c = (it >> 3) % CINP;
-        const int tap = (it >> 3) / CINP;
-        const int o = o0 + og * 8;
-        const bool ok = tap < KH * KW && c < a.Cin && o < a.Cout;
-        fv[t] = __builtin_amdgcn_raw_buffer_load_b128(
-            fr, ok ? (uint32_t)((((int64_t)tap * a.Cin + c) * a.Cout + o) * 2) : OOB, 0, 0);
-    }
-    // Bias of this lane's 8 output channels (zeros without bias).
-    const __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc(
-        a.bias ? (void *)a.bias : (void *)a.F, 0, a.bias ? a.Cout * 4 : 0, BUF_WORD3);
+    // 1. Filter slice and bias first.
+    FilterSlice<KH, KW, CS> filt;
+    filt.issue(a, o0, tid);
     u32x4 bq[NBW];
-#pragma unroll
-    for (int nb = 0; nb < NBW; ++nb)
-        bq[nb] = __builtin_amdgcn_raw_buffer_load_b128(
-            br, (uint32_t)((o0 + half * 32 + nb * 16 + (lane >> 4) * 4) * 4), 0, 0);
+    bias_issue(a, o0, half, lane, bq);
 
     // 2. The first D input rows of the band; the loop below keeps loading D
     //    rows ahead of use. The fence keeps the scheduler from hoisting these
@@ -216,51 +286,11 @@ void dense_rows_mfma(RowArgs a)
             xin[i][k] = __builtin_amdgcn_raw_buffer_load_b128(
                 xr, chunk_off<CINP>(a, y0 + i, tid + k * THREADS, rows_end), 0, 0);
 
-    // 3. Filter tile into LDS in its natural layout ft[tap][c][o], rows of
-    //    64 outputs padded to FPITCH elements: plain 16-byte writes.
-#pragma unroll
-    for (int t = 0; t < FITEMS; ++t) {
-        const int it = tid + t * THREADS;
-        const int og = it & 7;
-        const int c = (it >> 3) % CINP;
-        const int tap = (it >> 3) / CINP;
-        if (tap < KH * KW)
-            *reinterpret_cast<u32x4 *>(ft + (tap * CINP + c) * FPITCH + og * 8) = fv[t];
-    }
+    // 3. Filter slice into LDS, then 4. its A fragments into registers.
+    filt.commit(ft, tid);
     __syncthreads();
-
-    // 4. Filter fragments into registers with the gfx950 transpose read
-    //    (ds_read_b64_tr_b16). Within each 16-lane group, output lane i gets
-    //    element i % 4 of the 8-byte chunk addressed by lane 4j + i/4, for
-    //    j = 0..3. Lane r of the group therefore addresses row r/4, columns
-    //    4*(r%4)..+3 of a 4-row block of ft, and receives F[c0+j][o0+i]:
-    //    four consecutive input channels of one output channel, which is the
-    //    A-operand layout (lane holds 8 consecutive k of row o = lane % 16).
-    //    Two reads give the 8 channels of the lane's k-group.
     bf16x8 wf[KSTEPS][NBW];
-    {
-        const int g = lane >> 4;           // k-group: channels 8g..8g+7 of a 32-channel step
-        const int r = lane & 15;
-#pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks) {
-            const int tap = ks / CS;
-            const int cs = ks % CS;
-#pragma unroll
-            for (int nb = 0; nb < NBW; ++nb) {
-                i16x4 part[2];
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const int c = cs * 32 + g * 8 + h * 4 + (r >> 2);
-                    const int o = half * 32 + nb * 16 + 4 * (r & 3);
-                    part[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (__attribute__((address_space(3))) i16x4 *)(ft + (tap * CINP + c) * FPITCH + o));
-                }
-                const i16x8 both = {part[0][0], part[0][1], part[0][2], part[0][3],
-                                    part[1][0], part[1][1], part[1][2], part[1][3]};
-                wf[ks][nb] = __builtin_bit_cast(bf16x8, both);
-            }
-        }
-    }
+    FilterSlice<KH, KW, CS>::fragments(ft, lane, half, wf);
     __syncthreads();      // the staging area becomes the input-row area
 
     // 5. Input row 0 into LDS.
