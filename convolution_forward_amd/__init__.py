@@ -6,11 +6,14 @@ device memory and the current stream; nothing here computes on the CPU, and
 there is no fallback: if the library is not built, or a tensor is not on a
 GPU, the call raises.
 
-    conv2d_nhwc(x, f, bias=None, out=None, out_dtype=None)
+    conv2d_nhwc(x, f, bias=None, out=None, out_dtype=None, stride=1, padding=0, dilation=1, groups=1)
         Dense cross-correlation, X [N,H,W,Cin] (channel stride 1, other
-        strides free), F [KH,KW,Cin,Cout] contiguous -> Y [N,Ho,Wo,Cout].
+        strides free), F [KH,KW,Cin/groups,Cout] contiguous -> Y [N,Ho,Wo,Cout].
     conv_depthwise(x, w, bias=None, stride=1, padding=0, dilation=1, exact=True)
         Depthwise, X [N,C,H,W], w [C*mult,KH,KW] -> Y [N,C*mult,Ho,Wo].
+
+padding is an int (all sides), a pair (rows, columns; the same before and
+after), or four values (top, bottom, left, right).
 """
 from __future__ import annotations
 
@@ -39,9 +42,17 @@ VARIANT_AUTO = 0
 VARIANT_DIRECT = 1
 VARIANT_TILED = 2
 
-EXPORTED = ("conv2d_nhwc_fwd", "conv2d_nhwc_fwd_variant", "conv_depthwise_fwd", "conv_depthwise_fwd_variant",
-            "conv2d_nhwc_auto_variant", "conv_depthwise_auto_variant", "conv_out_size", "conv_status_str",
-            "conv_copy_bytes")
+EXPORTED = ("conv2d_nhwc_fwd", "conv2d_nhwc_fwd_variant", "conv2d_nhwc_fwd_window", "conv_depthwise_fwd",
+            "conv_depthwise_fwd_variant", "conv_depthwise_fwd_window", "conv2d_nhwc_auto_variant",
+            "conv2d_nhwc_window_auto_variant", "conv_depthwise_auto_variant", "conv_depthwise_window_auto_variant",
+            "conv_out_size", "conv_out_size_window", "conv_status_str", "conv_copy_bytes")
+
+
+class ConvWindow(ctypes.Structure):
+    """struct conv_window (include/convfwd.h)."""
+    _fields_ = [(name, ctypes.c_int) for name in
+                ("stride_h", "stride_w", "pad_top", "pad_bottom", "pad_left", "pad_right", "dil_h", "dil_w",
+                 "groups")]
 
 
 class ConvError(RuntimeError):
@@ -83,6 +94,17 @@ def load_library():
     lib.conv_depthwise_auto_variant.argtypes = [i] * 13
     lib.conv_out_size.restype = i64
     lib.conv_out_size.argtypes = [i64, i, i, i, i]
+    wp = ctypes.POINTER(ConvWindow)
+    lib.conv2d_nhwc_fwd_window.restype = i
+    lib.conv2d_nhwc_fwd_window.argtypes = [p, p, p, p, p, p] + [i] * 7 + [wp, i, i, i, p]
+    lib.conv_depthwise_fwd_window.restype = i
+    lib.conv_depthwise_fwd_window.argtypes = [p, p, p, p] + [i] * 7 + [wp, i, i, p]
+    lib.conv2d_nhwc_window_auto_variant.restype = i
+    lib.conv2d_nhwc_window_auto_variant.argtypes = [p, p] + [i] * 7 + [wp, i, i]
+    lib.conv_depthwise_window_auto_variant.restype = i
+    lib.conv_depthwise_window_auto_variant.argtypes = [i] * 7 + [wp]
+    lib.conv_out_size_window.restype = i64
+    lib.conv_out_size_window.argtypes = [i64, i, i, i, i, i]
     lib.conv_status_str.restype = ctypes.c_char_p
     lib.conv_status_str.argtypes = [i]
     lib.conv_copy_bytes.restype = i
@@ -108,11 +130,30 @@ def out_size(n: int, k: int, stride: int = 1, pad: int = 0, dil: int = 1) -> int
     return int(load_library().conv_out_size(n, k, stride, pad, dil))
 
 
+def out_size_window(n: int, k: int, stride: int = 1, pad_before: int = 0, pad_after: int = 0, dil: int = 1) -> int:
+    return int(load_library().conv_out_size_window(n, k, stride, pad_before, pad_after, dil))
+
+
 def _pair(v):
     if isinstance(v, (tuple, list)):
         a, b = v
         return int(a), int(b)
     return int(v), int(v)
+
+
+def _pads(padding):
+    """(top, bottom, left, right) from an int, a (rows, columns) pair or four values."""
+    if isinstance(padding, (tuple, list)) and len(padding) == 4:
+        return tuple(int(v) for v in padding)
+    ph, pw = _pair(padding)
+    return ph, ph, pw, pw
+
+
+def window(stride=1, padding=0, dilation=1, groups: int = 1) -> ConvWindow:
+    sh, sw = _pair(stride)
+    pt, pb, pl, pr = _pads(padding)
+    dh, dw = _pair(dilation)
+    return ConvWindow(sh, sw, pt, pb, pl, pr, dh, dw, int(groups))
 
 
 def _torch():
@@ -143,40 +184,43 @@ def _strides_arr(t):
     return (ctypes.c_int64 * 4)(*t.stride())
 
 
-def conv2d_nhwc(x, f, bias=None, out=None, out_dtype=None, variant: int = VARIANT_AUTO):
+def conv2d_nhwc(x, f, bias=None, out=None, out_dtype=None, variant: int = VARIANT_AUTO, stride=1, padding=0,
+                dilation=1, groups: int = 1):
     """Dense NHWC cross-correlation on the GPU (see include/convfwd.h)."""
     torch = _torch()
     lib = load_library()
     _require_gpu(x, f, bias, out)
     if x.dim() != 4 or f.dim() != 4:
-        raise ValueError("expected X as [N,H,W,Cin] and F as [KH,KW,Cin,Cout]")
+        raise ValueError("expected X as [N,H,W,Cin] and F as [KH,KW,Cin/groups,Cout]")
     N, H, W, Cin = x.shape
     KH, KW, Cf, Cout = f.shape
-    if Cf != Cin:
-        raise ValueError(f"filter input channels {Cf} != input channels {Cin}")
+    if groups < 1 or Cf * groups != Cin:
+        raise ValueError(f"filter input channels {Cf} x groups {groups} != input channels {Cin}")
     if f.dtype != x.dtype:
         raise ValueError("X and F must share a dtype")
     if not f.is_contiguous():
         raise ValueError("F must be contiguous [KH,KW,Cin,Cout]")
     if bias is not None and (bias.dtype != torch.float32 or not bias.is_contiguous() or bias.numel() != Cout):
         raise ValueError("bias must be a contiguous float32 tensor of Cout values")
-    Ho, Wo = H - KH + 1, W - KW + 1
+    win = window(stride, padding, dilation, groups)
+    Ho = out_size_window(H, KH, win.stride_h, win.pad_top, win.pad_bottom, win.dil_h)
+    Wo = out_size_window(W, KW, win.stride_w, win.pad_left, win.pad_right, win.dil_w)
     ydt = out.dtype if out is not None else (out_dtype or x.dtype)
     if out is None:
         if Ho <= 0 or Wo <= 0 or min(N, H, W, Cin, KH, KW, Cout) <= 0:
             # Let the library classify the error; no output buffer is needed.
-            st = lib.conv2d_nhwc_fwd_variant(x.data_ptr() or 1, _strides_arr(x), f.data_ptr() or 1, None, 1,
-                                             None, N, H, W, Cin, KH, KW, Cout, _dtype_code(x.dtype),
-                                             _dtype_code(ydt), variant, None)
-            _check(st if st != CONV_OK else CONV_ERR_SHAPE, "conv2d_nhwc_fwd")
+            st = lib.conv2d_nhwc_fwd_window(x.data_ptr() or 1, _strides_arr(x), f.data_ptr() or 1, None, 1,
+                                            None, N, H, W, Cin, KH, KW, Cout, ctypes.byref(win),
+                                            _dtype_code(x.dtype), _dtype_code(ydt), variant, None)
+            _check(st if st != CONV_OK else CONV_ERR_SHAPE, "conv2d_nhwc_fwd_window")
         out = torch.empty((N, Ho, Wo, Cout), dtype=ydt, device=x.device)
     elif tuple(out.shape) != (N, Ho, Wo, Cout):
         raise ValueError(f"out has shape {tuple(out.shape)}, expected {(N, Ho, Wo, Cout)}")
-    st = lib.conv2d_nhwc_fwd_variant(x.data_ptr(), _strides_arr(x), f.data_ptr(),
-                                     None if bias is None else bias.data_ptr(), out.data_ptr(), _strides_arr(out),
-                                     N, H, W, Cin, KH, KW, Cout, _dtype_code(x.dtype), _dtype_code(out.dtype),
-                                     variant, _stream_ptr(x.device))
-    _check(st, "conv2d_nhwc_fwd")
+    st = lib.conv2d_nhwc_fwd_window(x.data_ptr(), _strides_arr(x), f.data_ptr(),
+                                    None if bias is None else bias.data_ptr(), out.data_ptr(), _strides_arr(out),
+                                    N, H, W, Cin, KH, KW, Cout, ctypes.byref(win), _dtype_code(x.dtype),
+                                    _dtype_code(out.dtype), variant, _stream_ptr(x.device))
+    _check(st, "conv2d_nhwc_fwd_window")
     return out
 
 
@@ -199,43 +243,42 @@ def conv_depthwise(x, w, bias=None, stride=1, padding=0, dilation=1, exact: bool
     mult = Cout // C
     if bias is not None and (bias.dtype != torch.float32 or not bias.is_contiguous() or bias.numel() != Cout):
         raise ValueError("bias must be a contiguous float32 tensor of C*multiplier values")
-    sh, sw = _pair(stride)
-    ph, pw = _pair(padding)
-    dh, dw = _pair(dilation)
-    Ho, Wo = out_size(H, KH, sh, ph, dh), out_size(W, KW, sw, pw, dw)
+    win = window(stride, padding, dilation)
+    Ho = out_size_window(H, KH, win.stride_h, win.pad_top, win.pad_bottom, win.dil_h)
+    Wo = out_size_window(W, KW, win.stride_w, win.pad_left, win.pad_right, win.dil_w)
     mode = CONV_DW_EXACT if exact else CONV_DW_FAST
     if out is None:
         if Ho <= 0 or Wo <= 0:
             # Let the library classify the error (it returns before touching
             # any pointer); no output buffer is needed.
-            st = lib.conv_depthwise_fwd_variant(x.data_ptr() or 1, w.data_ptr() or 1, None, 1, N, C, H, W, mult,
-                                                KH, KW, sh, sw, ph, pw, dh, dw, mode, variant, None)
-            _check(st if st != CONV_OK else CONV_ERR_SHAPE, "conv_depthwise_fwd")
+            st = lib.conv_depthwise_fwd_window(x.data_ptr() or 1, w.data_ptr() or 1, None, 1, N, C, H, W, mult,
+                                               KH, KW, ctypes.byref(win), mode, variant, None)
+            _check(st if st != CONV_OK else CONV_ERR_SHAPE, "conv_depthwise_fwd_window")
         out = torch.empty((N, Cout, Ho, Wo), dtype=torch.float32, device=x.device)
     elif tuple(out.shape) != (N, Cout, Ho, Wo) or not out.is_contiguous() or out.dtype != torch.float32:
         raise ValueError(f"out must be a contiguous float32 tensor of shape {(N, Cout, Ho, Wo)}")
-    st = lib.conv_depthwise_fwd_variant(x.data_ptr(), w.data_ptr(), None if bias is None else bias.data_ptr(),
-                                        out.data_ptr(), N, C, H, W, mult, KH, KW, sh, sw, ph, pw, dh, dw, mode,
-                                        variant, _stream_ptr(x.device))
-    _check(st, "conv_depthwise_fwd")
+    st = lib.conv_depthwise_fwd_window(x.data_ptr(), w.data_ptr(), None if bias is None else bias.data_ptr(),
+                                       out.data_ptr(), N, C, H, W, mult, KH, KW, ctypes.byref(win), mode, variant,
+                                       _stream_ptr(x.device))
+    _check(st, "conv_depthwise_fwd_window")
     return out
 
 
-def dense_variant_for(x, f, out_dtype=None) -> int:
+def dense_variant_for(x, f, out_dtype=None, stride=1, padding=0, dilation=1, groups: int = 1) -> int:
     """The variant CONV_VARIANT_AUTO launches for these tensors (host query)."""
     N, H, W, Cin = x.shape
     KH, KW, _, Cout = f.shape
-    return int(load_library().conv2d_nhwc_auto_variant(_strides_arr(x), x.data_ptr(), N, H, W, Cin, KH, KW, Cout,
-                                                       _dtype_code(x.dtype), _dtype_code(out_dtype or x.dtype)))
+    win = window(stride, padding, dilation, groups)
+    return int(load_library().conv2d_nhwc_window_auto_variant(
+        _strides_arr(x), x.data_ptr(), N, H, W, Cin, KH, KW, Cout, ctypes.byref(win), _dtype_code(x.dtype),
+        _dtype_code(out_dtype or x.dtype)))
 
 
 def depthwise_variant_for(shape_x, shape_w, stride=1, padding=0, dilation=1) -> int:
     N, C, H, W = shape_x
     Cout, KH, KW = shape_w
-    sh, sw = _pair(stride)
-    ph, pw = _pair(padding)
-    dh, dw = _pair(dilation)
-    return int(load_library().conv_depthwise_auto_variant(N, C, H, W, Cout // C, KH, KW, sh, sw, ph, pw, dh, dw))
+    win = window(stride, padding, dilation)
+    return int(load_library().conv_depthwise_window_auto_variant(N, C, H, W, Cout // C, KH, KW, ctypes.byref(win)))
 
 
 def copy_bytes(src, dst, nbytes: int | None = None):

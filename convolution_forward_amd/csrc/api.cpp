@@ -42,20 +42,31 @@ bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
 // int, so four of them fit, but stride arithmetic is checked separately.
 bool stride_ok(int64_t s) { return s >= 0 && s <= (int64_t(1) << 40); }
 
-// Shape, dtype and layout checks (no pointer checks); fills p except pointers.
+// The lecture's restricted window: unit stride, no padding, one group.
+constexpr conv_window PLAIN_WINDOW = {1, 1, 0, 0, 0, 0, 1, 1, 1};
+
+// Shape, window, dtype and layout checks (no pointer checks); fills p
+// except pointers.
 conv_status check_dense_shape(const int64_t *x_strides, const int64_t *y_strides, int N, int H, int W,
-                              int Cin, int KH, int KW, int Cout, conv_dtype x_dtype, conv_dtype y_dtype,
-                              DenseProblem *p)
+                              int Cin, int KH, int KW, int Cout, const conv_window &win, conv_dtype x_dtype,
+                              conv_dtype y_dtype, DenseProblem *p)
 {
     if (N <= 0 || H <= 0 || W <= 0 || Cin <= 0 || KH <= 0 || KW <= 0 || Cout <= 0)
         return CONV_ERR_NONPOSITIVE;
-    if (KH > H || KW > W)
+    if (win.stride_h < 1 || win.stride_w < 1 || win.dil_h < 1 || win.dil_w < 1 || win.groups < 1 ||
+        win.pad_top < 0 || win.pad_bottom < 0 || win.pad_left < 0 || win.pad_right < 0)
+        return CONV_ERR_NONPOSITIVE;
+    const int64_t Ho64 = conv_out_size_window(H, KH, win.stride_h, win.pad_top, win.pad_bottom, win.dil_h);
+    const int64_t Wo64 = conv_out_size_window(W, KW, win.stride_w, win.pad_left, win.pad_right, win.dil_w);
+    if (Ho64 <= 0 || Wo64 <= 0 || Cin % win.groups != 0 || Cout % win.groups != 0)
         return CONV_ERR_SHAPE;
+    if (Ho64 > INT_MAX || Wo64 > INT_MAX)
+        return CONV_ERR_UNSUPPORTED;
     if (!dtype_known(x_dtype) || !dtype_known(y_dtype))
         return CONV_ERR_DTYPE;
     if (x_dtype == CONV_F32 && y_dtype == CONV_BF16)
         return CONV_ERR_DTYPE;
-    const int Ho = H - KH + 1, Wo = W - KW + 1;
+    const int Ho = (int)Ho64, Wo = (int)Wo64;
 
     int64_t xs[4], ys[4];
     if (x_strides) {
@@ -110,23 +121,32 @@ conv_status check_dense_shape(const int64_t *x_strides, const int64_t *y_strides
     p->Wo = Wo;
     p->xdt = x_dtype;
     p->ydt = y_dtype;
+    p->sh = win.stride_h;
+    p->sw = win.stride_w;
+    p->pt = win.pad_top;
+    p->pl = win.pad_left;
+    p->dh = win.dil_h;
+    p->dw = win.dil_w;
+    p->groups = win.groups;
     return CONV_OK;
 }
 
 conv_status validate_dense(const void *X, const int64_t *x_strides, const void *F, const float *bias,
                            void *Y, const int64_t *y_strides, int N, int H, int W, int Cin, int KH,
-                           int KW, int Cout, conv_dtype x_dtype, conv_dtype y_dtype, DenseProblem *p)
+                           int KW, int Cout, const conv_window &win, conv_dtype x_dtype, conv_dtype y_dtype,
+                           DenseProblem *p)
 {
     if (!X || !F || !Y)
         return CONV_ERR_NULL;
-    conv_status st = check_dense_shape(x_strides, y_strides, N, H, W, Cin, KH, KW, Cout, x_dtype, y_dtype, p);
+    conv_status st =
+        check_dense_shape(x_strides, y_strides, N, H, W, Cin, KH, KW, Cout, win, x_dtype, y_dtype, p);
     if (st != CONV_OK)
         return st;
     const int64_t xdims[4] = {N, H, W, Cin};
     const int64_t ydims[4] = {N, p->Ho, p->Wo, Cout};
     const Range ry = strided_range(Y, ydims, p->ys, dtype_size(y_dtype));
     if (overlaps(ry, strided_range(X, xdims, p->xs, dtype_size(x_dtype))) ||
-        overlaps(ry, flat_range(F, (int64_t)KH * KW * Cin * Cout * dtype_size(x_dtype))) ||
+        overlaps(ry, flat_range(F, (int64_t)KH * KW * (Cin / win.groups) * Cout * dtype_size(x_dtype))) ||
         (bias && overlaps(ry, flat_range(bias, (int64_t)Cout * 4))))
         return CONV_ERR_ALIAS;
     p->X = X;
@@ -139,6 +159,8 @@ conv_status validate_dense(const void *X, const int64_t *x_strides, const void *
 // The tiled (matrix-core) variant: one kernel family per operand type.
 bool dense_tiled_supports(const DenseProblem &p)
 {
+    if (!plain_window(p))
+        return false;
     return p.xdt == CONV_BF16 ? dense_mfma_bf16_supports(p) : dense_mfma_f32_supports(p);
 }
 
@@ -150,18 +172,20 @@ hipError_t launch_dense_tiled(const DenseProblem &p, hipStream_t s)
 int dense_auto(const DenseProblem &p) { return dense_tiled_supports(p) ? CONV_VARIANT_TILED : CONV_VARIANT_DIRECT; }
 
 // Shape and mode checks (no pointer checks); fills p except pointers.
-conv_status check_dw_shape(int N, int C, int H, int W, int mult, int KH, int KW, int sh, int sw, int ph, int pw,
-                           int dh, int dw, conv_dw_mode mode, DwProblem *p)
+conv_status check_dw_shape(int N, int C, int H, int W, int mult, int KH, int KW, int sh, int sw, int ph, int pb,
+                           int pw, int pr, int dh, int dw, conv_dw_mode mode, DwProblem *p)
 {
     if (N <= 0 || C <= 0 || H <= 0 || W <= 0 || mult <= 0 || KH <= 0 || KW <= 0 || sh < 1 || sw < 1 ||
-        dh < 1 || dw < 1 || ph < 0 || pw < 0)
+        dh < 1 || dw < 1 || ph < 0 || pw < 0 || pb < 0 || pr < 0)
         return CONV_ERR_NONPOSITIVE;
     if (mode != CONV_DW_EXACT && mode != CONV_DW_FAST)
         return CONV_ERR_UNSUPPORTED;
-    const int64_t Ho = conv_out_size(H, KH, sh, ph, dh);
-    const int64_t Wo = conv_out_size(W, KW, sw, pw, dw);
+    const int64_t Ho = conv_out_size_window(H, KH, sh, ph, pb, dh);
+    const int64_t Wo = conv_out_size_window(W, KW, sw, pw, pr, dw);
     if (Ho <= 0 || Wo <= 0)
         return CONV_ERR_SHAPE;
+    if (Ho > INT_MAX || Wo > INT_MAX)
+        return CONV_ERR_UNSUPPORTED;
     if ((int64_t)C * mult > INT_MAX)
         return CONV_ERR_UNSUPPORTED;
     p->X = nullptr;
@@ -179,6 +203,8 @@ conv_status check_dw_shape(int N, int C, int H, int W, int mult, int KH, int KW,
     p->sw = sw;
     p->ph = ph;
     p->pw = pw;
+    p->pb = pb;
+    p->pr = pr;
     p->dh = dh;
     p->dw = dw;
     p->Ho = (int)Ho;
@@ -188,12 +214,12 @@ conv_status check_dw_shape(int N, int C, int H, int W, int mult, int KH, int KW,
 }
 
 conv_status validate_dw(const float *X, const float *w, const float *bias, float *Y, int N, int C, int H,
-                        int W, int mult, int KH, int KW, int sh, int sw, int ph, int pw, int dh, int dw,
-                        conv_dw_mode mode, DwProblem *p)
+                        int W, int mult, int KH, int KW, int sh, int sw, int ph, int pb, int pw, int pr, int dh,
+                        int dw, conv_dw_mode mode, DwProblem *p)
 {
     if (!X || !w || !Y)
         return CONV_ERR_NULL;
-    conv_status st = check_dw_shape(N, C, H, W, mult, KH, KW, sh, sw, ph, pw, dh, dw, mode, p);
+    conv_status st = check_dw_shape(N, C, H, W, mult, KH, KW, sh, sw, ph, pb, pw, pr, dh, dw, mode, p);
     if (st != CONV_OK)
         return st;
     const int64_t Cout = (int64_t)C * mult;
@@ -232,6 +258,17 @@ int64_t conv_out_size(int64_t in, int k, int stride, int pad, int dil)
     return span / stride + 1;
 }
 
+int64_t conv_out_size_window(int64_t in, int k, int stride, int pad_before, int pad_after, int dil)
+{
+    if (in <= 0 || k <= 0 || stride <= 0 || pad_before < 0 || pad_after < 0 || dil <= 0)
+        return 0;
+    const int64_t eff = (int64_t)dil * (k - 1) + 1;
+    const int64_t span = in + (int64_t)pad_before + pad_after - eff;
+    if (span < 0)
+        return 0;
+    return span / stride + 1;
+}
+
 const char *conv_status_str(conv_status s)
 {
     switch (s) {
@@ -248,14 +285,16 @@ const char *conv_status_str(conv_status s)
     return "unknown status";
 }
 
-conv_status conv2d_nhwc_fwd_variant(const void *X, const int64_t *x_strides, const void *F,
-                                    const float *bias, void *Y, const int64_t *y_strides, int N, int H,
-                                    int W, int Cin, int KH, int KW, int Cout, conv_dtype x_dtype,
-                                    conv_dtype y_dtype, int variant, void *stream)
+conv_status conv2d_nhwc_fwd_window(const void *X, const int64_t *x_strides, const void *F, const float *bias,
+                                   void *Y, const int64_t *y_strides, int N, int H, int W, int Cin, int KH, int KW,
+                                   int Cout, const conv_window *win, conv_dtype x_dtype, conv_dtype y_dtype,
+                                   int variant, void *stream)
 {
+    if (!win)
+        return CONV_ERR_NULL;
     DenseProblem p;
-    conv_status st = validate_dense(X, x_strides, F, bias, Y, y_strides, N, H, W, Cin, KH, KW, Cout, x_dtype,
-                                    y_dtype, &p);
+    conv_status st = validate_dense(X, x_strides, F, bias, Y, y_strides, N, H, W, Cin, KH, KW, Cout, *win,
+                                    x_dtype, y_dtype, &p);
     if (st != CONV_OK)
         return st;
     if (variant == CONV_VARIANT_AUTO)
@@ -273,6 +312,16 @@ conv_status conv2d_nhwc_fwd_variant(const void *X, const int64_t *x_strides, con
     }
 }
 
+conv_status conv2d_nhwc_fwd_variant(const void *X, const int64_t *x_strides, const void *F,
+                                    const float *bias, void *Y, const int64_t *y_strides, int N, int H,
+                                    int W, int Cin, int KH, int KW, int Cout, conv_dtype x_dtype,
+                                    conv_dtype y_dtype, int variant, void *stream)
+{
+    // The lecture's precondition K <= min(H, W) is the window's Ho, Wo >= 1.
+    return conv2d_nhwc_fwd_window(X, x_strides, F, bias, Y, y_strides, N, H, W, Cin, KH, KW, Cout, &PLAIN_WINDOW,
+                                  x_dtype, y_dtype, variant, stream);
+}
+
 conv_status conv2d_nhwc_fwd(const void *X, const int64_t *x_strides, const void *F, const float *bias,
                             void *Y, const int64_t *y_strides, int N, int H, int W, int Cin, int KH,
                             int KW, int Cout, conv_dtype x_dtype, conv_dtype y_dtype, void *stream)
@@ -281,24 +330,37 @@ conv_status conv2d_nhwc_fwd(const void *X, const int64_t *x_strides, const void 
                                    y_dtype, CONV_VARIANT_AUTO, stream);
 }
 
-int conv2d_nhwc_auto_variant(const int64_t *x_strides, const void *X, int N, int H, int W, int Cin, int KH,
-                             int KW, int Cout, conv_dtype x_dtype, conv_dtype y_dtype)
+int conv2d_nhwc_window_auto_variant(const int64_t *x_strides, const void *X, int N, int H, int W, int Cin, int KH,
+                                    int KW, int Cout, const conv_window *win, conv_dtype x_dtype,
+                                    conv_dtype y_dtype)
 {
     DenseProblem p;
-    if (check_dense_shape(x_strides, nullptr, N, H, W, Cin, KH, KW, Cout, x_dtype, y_dtype, &p) != CONV_OK)
+    if (!win || check_dense_shape(x_strides, nullptr, N, H, W, Cin, KH, KW, Cout, *win, x_dtype, y_dtype, &p) !=
+                    CONV_OK)
         return -1;
     p.X = X;    // only its alignment is looked at
     return dense_auto(p);
 }
 
-conv_status conv_depthwise_fwd_variant(const float *X, const float *w, const float *bias, float *Y, int N,
-                                       int C, int H, int W, int multiplier, int KH, int KW, int stride_h,
-                                       int stride_w, int pad_h, int pad_w, int dil_h, int dil_w,
-                                       conv_dw_mode mode, int variant, void *stream)
+int conv2d_nhwc_auto_variant(const int64_t *x_strides, const void *X, int N, int H, int W, int Cin, int KH,
+                             int KW, int Cout, conv_dtype x_dtype, conv_dtype y_dtype)
 {
+    return conv2d_nhwc_window_auto_variant(x_strides, X, N, H, W, Cin, KH, KW, Cout, &PLAIN_WINDOW, x_dtype,
+                                           y_dtype);
+}
+
+conv_status conv_depthwise_fwd_window(const float *X, const float *w, const float *bias, float *Y, int N, int C,
+                                      int H, int W, int multiplier, int KH, int KW, const conv_window *win,
+                                      conv_dw_mode mode, int variant, void *stream)
+{
+    if (!win)
+        return CONV_ERR_NULL;
+    if (win->groups != 1)
+        return CONV_ERR_UNSUPPORTED;
     DwProblem p;
-    conv_status st = validate_dw(X, w, bias, Y, N, C, H, W, multiplier, KH, KW, stride_h, stride_w, pad_h, pad_w,
-                                 dil_h, dil_w, mode, &p);
+    conv_status st = validate_dw(X, w, bias, Y, N, C, H, W, multiplier, KH, KW, win->stride_h, win->stride_w,
+                                 win->pad_top, win->pad_bottom, win->pad_left, win->pad_right, win->dil_h,
+                                 win->dil_w, mode, &p);
     if (st != CONV_OK)
         return st;
     if (variant == CONV_VARIANT_AUTO)
@@ -316,6 +378,15 @@ conv_status conv_depthwise_fwd_variant(const float *X, const float *w, const flo
     }
 }
 
+conv_status conv_depthwise_fwd_variant(const float *X, const float *w, const float *bias, float *Y, int N,
+                                       int C, int H, int W, int multiplier, int KH, int KW, int stride_h,
+                                       int stride_w, int pad_h, int pad_w, int dil_h, int dil_w,
+                                       conv_dw_mode mode, int variant, void *stream)
+{
+    const conv_window win = {stride_h, stride_w, pad_h, pad_h, pad_w, pad_w, dil_h, dil_w, 1};
+    return conv_depthwise_fwd_window(X, w, bias, Y, N, C, H, W, multiplier, KH, KW, &win, mode, variant, stream);
+}
+
 conv_status conv_depthwise_fwd(const float *X, const float *w, const float *bias, float *Y, int N, int C, int H,
                                int W, int multiplier, int KH, int KW, int stride_h, int stride_w, int pad_h,
                                int pad_w, int dil_h, int dil_w, conv_dw_mode mode, void *stream)
@@ -324,14 +395,22 @@ conv_status conv_depthwise_fwd(const float *X, const float *w, const float *bias
                                       pad_w, dil_h, dil_w, mode, CONV_VARIANT_AUTO, stream);
 }
 
+int conv_depthwise_window_auto_variant(int N, int C, int H, int W, int multiplier, int KH, int KW,
+                                       const conv_window *win)
+{
+    DwProblem p;
+    if (!win || win->groups != 1 ||
+        check_dw_shape(N, C, H, W, multiplier, KH, KW, win->stride_h, win->stride_w, win->pad_top, win->pad_bottom,
+                       win->pad_left, win->pad_right, win->dil_h, win->dil_w, CONV_DW_EXACT, &p) != CONV_OK)
+        return -1;
+    return dw_auto(p);
+}
+
 int conv_depthwise_auto_variant(int N, int C, int H, int W, int multiplier, int KH, int KW, int stride_h,
                                 int stride_w, int pad_h, int pad_w, int dil_h, int dil_w)
 {
-    DwProblem p;
-    if (check_dw_shape(N, C, H, W, multiplier, KH, KW, stride_h, stride_w, pad_h, pad_w, dil_h, dil_w,
-                       CONV_DW_EXACT, &p) != CONV_OK)
-        return -1;
-    return dw_auto(p);
+    const conv_window win = {stride_h, stride_w, pad_h, pad_h, pad_w, pad_w, dil_h, dil_w, 1};
+    return conv_depthwise_window_auto_variant(N, C, H, W, multiplier, KH, KW, &win);
 }
 
 conv_status conv_copy_bytes(const void *src, void *dst, int64_t bytes, void *stream)

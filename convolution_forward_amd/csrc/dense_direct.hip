@@ -2,9 +2,16 @@
 //
 // "CMU DLSys Lecture 14: Convolutional Network Implementation", section 1:
 // Y[n,y,x,o] = sum over (i,j,c) of X[n,y+i,x+j,c] * F[i,j,c,o], no flip.
+// The same loops take the window of "Convolution Is Wx+b Moving Across a
+// Signal" (section "Why 1D? Why 2D?"): output (y, x) reads input row
+// y*sh + i*dh - pt and column x*sw + j*dw - pl, zero outside the input; and
+// groups (section "Find the same sum in CKE's C kernels"): output channel o
+// sums over the Cin/groups input channels of its group only, with F of shape
+// [KH,KW,Cin/groups,Cout].
 // This is the variant that takes every legal shape and stride: threads are
 // laid out with o fastest, so F and Y accesses are coalesced along Cout and X
-// is read as a broadcast. fp32 accumulation in (i,j,c) order.
+// is read as a broadcast. fp32 accumulation in (i,j,c) order; a padding
+// position contributes 0 * F like any other tap.
 #include "common.h"
 #include "internal.h"
 
@@ -17,7 +24,8 @@ struct DirectArgs {
     const float *bias;
     void *Y;
     int64_t xs0, xs1, xs2, ys0, ys1, ys2;
-    int Cin, KH, KW, Cout, Ho, Wo;
+    int H, W, Cin, KH, KW, Cout, Ho, Wo;
+    int sh, sw, pt, pl, dh, dw, groups;
     int64_t total;
 };
 
@@ -35,13 +43,20 @@ __global__ __launch_bounds__(256) void dense_direct_kernel(DirectArgs a)
         r /= a.Wo;
         const int y = (int)(r % a.Ho);
         const int64_t n = r / a.Ho;
+        const int cg = a.Cin / a.groups;                 // input channels per group
+        const int c0 = o / (a.Cout / a.groups) * cg;     // first input channel of o's group
         float acc = 0.0f;
         for (int i = 0; i < a.KH; ++i) {
+            const int r = y * a.sh + i * a.dh - a.pt;
             for (int j = 0; j < a.KW; ++j) {
-                const TX *xp = X + n * a.xs0 + (int64_t)(y + i) * a.xs1 + (int64_t)(x + j) * a.xs2;
-                const TX *fp = F + ((int64_t)(i * a.KW + j) * a.Cin) * a.Cout + o;
-                for (int c = 0; c < a.Cin; ++c)
-                    acc = __builtin_fmaf(load_as_f32(xp + c), load_as_f32(fp + (int64_t)c * a.Cout), acc);
+                const int col = x * a.sw + j * a.dw - a.pl;
+                const bool in = r >= 0 && r < a.H && col >= 0 && col < a.W;
+                const TX *xp = X + n * a.xs0 + (int64_t)(in ? r : 0) * a.xs1 + (int64_t)(in ? col : 0) * a.xs2 + c0;
+                const TX *fp = F + ((int64_t)(i * a.KW + j) * cg) * a.Cout + o;
+                for (int c = 0; c < cg; ++c) {
+                    const float xv = in ? load_as_f32(xp + c) : 0.0f;
+                    acc = __builtin_fmaf(xv, load_as_f32(fp + (int64_t)c * a.Cout), acc);
+                }
             }
         }
         if (a.bias)
@@ -65,6 +80,15 @@ hipError_t launch_dense_direct(const DenseProblem &p, hipStream_t s)
     a.ys0 = p.ys[0];
     a.ys1 = p.ys[1];
     a.ys2 = p.ys[2];
+    a.H = p.H;
+    a.W = p.W;
+    a.sh = p.sh;
+    a.sw = p.sw;
+    a.pt = p.pt;
+    a.pl = p.pl;
+    a.dh = p.dh;
+    a.dw = p.dw;
+    a.groups = p.groups;
     a.Cin = p.Cin;
     a.KH = p.KH;
     a.KW = p.KW;

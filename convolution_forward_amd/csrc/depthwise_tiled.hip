@@ -280,7 +280,8 @@ bool plan(const DwProblem &p, TilePlan &out)
         return false;
     if (p.sh != p.sw || (p.sh != 1 && p.sh != 2) || p.dh != 1 || p.dw != 1)
         return false;
-    if (p.ph > MAX_PAD || p.pw > MAX_PAD || p.ph >= p.KH || p.pw >= p.KW || p.Wo > THREADS)
+    if (p.ph > MAX_PAD || p.pw > MAX_PAD || p.ph >= p.KH || p.pw >= p.KW || p.pb >= p.KH || p.pr >= p.KW ||
+        p.Wo > THREADS)
         return false;       // every output window must overlap the input
     if (p.sh == 2 && (p.W % 2) != 0)
         return false;       // phase planes need even rows

@@ -19,7 +19,19 @@ struct DenseProblem {
     int64_t ys[4];
     int N, H, W, Cin, KH, KW, Cout, Ho, Wo;
     conv_dtype xdt, ydt;
+    // Window: stride, padding before each axis (the padding after only
+    // shapes Ho and Wo), dilation, groups. The lecture's operator is
+    // sh = sw = dh = dw = groups = 1, pt = pl = 0.
+    int sh, sw, pt, pl, dh, dw, groups;
 };
+
+// True for the lecture's restricted operator (unit stride, no padding, no
+// dilation, one group).
+inline bool plain_window(const DenseProblem &p)
+{
+    return p.sh == 1 && p.sw == 1 && p.pt == 0 && p.pl == 0 && p.dh == 1 && p.dw == 1 && p.groups == 1 &&
+           p.Ho == p.H - p.KH + 1 && p.Wo == p.W - p.KW + 1;
+}
 
 // A validated depthwise problem: contiguous NCHW X, [C*mult,KH,KW] w, NCHW Y.
 struct DwProblem {
@@ -28,6 +40,7 @@ struct DwProblem {
     const float *bias;
     float *Y;
     int N, C, H, W, mult, KH, KW, sh, sw, ph, pw, dh, dw, Ho, Wo;
+    int pb, pr;         // padding after each axis (ph, pw are the padding before)
     conv_dw_mode mode;
 };
 

@@ -155,6 +155,61 @@ CONVFWD_API conv_status conv_depthwise_fwd_variant(const float *X, const float *
                                        int stride_w, int pad_h, int pad_w, int dil_h, int dil_w,
                                        conv_dw_mode mode, int variant, void *stream);
 
+/*
+ * conv_window -- the window of a convolution beyond the lecture's restricted
+ * operator. "Convolution Is Wx+b Moving Across a Signal", section "Why 1D?
+ * Why 2D?", defines stride, zero padding and dilation per axis (the output
+ * size rule of conv_out_size_window); its section "Find the same sum in
+ * CKE's C kernels" sums, for one output channel, over the taps of its group
+ * of input channels only; its section "Where this shows up in models I work
+ * with" names causal Conv1D, which is padding placed entirely before the
+ * signal (pad_left = dil_w*(KW-1), pad_right = 0).
+ *
+ * Output row y reads input rows y*stride_h + i*dil_h - pad_top (i < KH) and
+ * columns x*stride_w + j*dil_w - pad_left (j < KW); positions outside the
+ * input read zero.
+ */
+typedef struct conv_window {
+    int stride_h, stride_w;     /* >= 1 */
+    int pad_top, pad_bottom;    /* zero rows before / after the input, >= 0 */
+    int pad_left, pad_right;    /* zero columns before / after the input, >= 0 */
+    int dil_h, dil_w;           /* >= 1 */
+    int groups;                 /* dense: >= 1 and divides Cin and Cout; depthwise: must be 1 */
+} conv_window;
+
+/*
+ * conv2d_nhwc_fwd_window -- dense forward cross-correlation with a window.
+ *
+ * Arguments as conv2d_nhwc_fwd, plus `win` (host pointer, not NULL). With
+ * groups = g the filter is [KH,KW,Cin/g,Cout] (contiguous) and output
+ * channel o belongs to group o / (Cout/g), reading input channels
+ * [(o / (Cout/g)) * Cin/g, ... + Cin/g). Ho and Wo follow
+ * conv_out_size_window. With stride 1, no padding, dilation 1 and one group
+ * this is conv2d_nhwc_fwd.
+ *
+ * Errors: as conv2d_nhwc_fwd; CONV_ERR_NULL also for win NULL;
+ * CONV_ERR_NONPOSITIVE for a stride, dilation or group count < 1 or a pad
+ * < 0; CONV_ERR_SHAPE when Ho or Wo <= 0 or groups does not divide Cin and
+ * Cout.
+ */
+CONVFWD_API conv_status conv2d_nhwc_fwd_window(const void *X, const int64_t *x_strides, const void *F,
+                                   const float *bias, void *Y, const int64_t *y_strides, int N, int H, int W,
+                                   int Cin, int KH, int KW, int Cout, const conv_window *win,
+                                   conv_dtype x_dtype, conv_dtype y_dtype, int variant, void *stream);
+
+/*
+ * conv_depthwise_fwd_window -- depthwise forward convolution with a window
+ * whose padding may differ before and after each axis (win->groups must be
+ * 1: the depthwise grouping is implied). Same contract, modes, layouts and
+ * errors as conv_depthwise_fwd, with xpad holding pad_top / pad_bottom rows
+ * and pad_left / pad_right columns of zeros; Ho and Wo follow
+ * conv_out_size_window. CONV_ERR_NULL also for win NULL; CONV_ERR_UNSUPPORTED
+ * for groups != 1.
+ */
+CONVFWD_API conv_status conv_depthwise_fwd_window(const float *X, const float *w, const float *bias, float *Y, int N,
+                                      int C, int H, int W, int multiplier, int KH, int KW,
+                                      const conv_window *win, conv_dw_mode mode, int variant, void *stream);
+
 /* Which variant CONV_VARIANT_AUTO would launch for these dense / depthwise
  * arguments (a CONV_VARIANT_* value), or -1 if the arguments are invalid.
  * Host-only; makes no HIP call. */
@@ -163,10 +218,20 @@ CONVFWD_API int conv2d_nhwc_auto_variant(const int64_t *x_strides, const void *X
 CONVFWD_API int conv_depthwise_auto_variant(int N, int C, int H, int W, int multiplier, int KH, int KW, int stride_h,
                                 int stride_w, int pad_h, int pad_w, int dil_h, int dil_w);
 
+CONVFWD_API int conv2d_nhwc_window_auto_variant(const int64_t *x_strides, const void *X, int N, int H, int W,
+                                    int Cin, int KH, int KW, int Cout, const conv_window *win,
+                                    conv_dtype x_dtype, conv_dtype y_dtype);
+CONVFWD_API int conv_depthwise_window_auto_variant(int N, int C, int H, int W, int multiplier, int KH, int KW,
+                                       const conv_window *win);
+
 /* Output size along one axis: floor((in + 2*pad - (dil*(k-1)+1)) / stride) + 1
  * ("Convolution Is Wx+b Moving Across a Signal", section "Why 1D? Why 2D?").
  * Returns a value <= 0 when no window fits or an argument is out of range. */
 CONVFWD_API int64_t conv_out_size(int64_t in, int k, int stride, int pad, int dil);
+
+/* The same rule with padding that differs before and after the axis:
+ * floor((in + pad_before + pad_after - (dil*(k-1)+1)) / stride) + 1. */
+CONVFWD_API int64_t conv_out_size_window(int64_t in, int k, int stride, int pad_before, int pad_after, int dil);
 
 /* Static, NUL-terminated description of a status code. */
 CONVFWD_API const char *conv_status_str(conv_status s);

@@ -166,3 +166,63 @@ def test_binding_rejects_cpu_tensors(lib):
         cf.conv2d_nhwc(x, f)
     with pytest.raises(ValueError):
         cf.conv_depthwise(torch.zeros(1, 2, 4, 4), torch.zeros(2, 3, 3))
+
+
+def test_window_entry_points(lib):
+    """The window entry points: the same argument classes, checked before any
+    HIP call (fake device addresses are never dereferenced)."""
+    XA, FA, YA = 0x10000000, 0x20000000, 0x30000000
+    W = cf.window
+    call = lambda win, **k: lib.conv2d_nhwc_fwd_window(
+        XA, None, FA, None, YA, None, k.get("N", 1), k.get("H", 8), k.get("Wd", 8), k.get("Cin", 6),
+        k.get("KH", 3), k.get("KW", 3), k.get("Cout", 6), ctypes.byref(win) if win is not None else None,
+        cf.CONV_F32, cf.CONV_F32, cf.VARIANT_AUTO, None)
+    assert call(None) == cf.CONV_ERR_NULL
+    assert call(W(stride=0)) == cf.CONV_ERR_NONPOSITIVE
+    assert call(W(dilation=(1, 0))) == cf.CONV_ERR_NONPOSITIVE
+    assert call(W(padding=(0, 0, -1, 0))) == cf.CONV_ERR_NONPOSITIVE
+    assert call(W(groups=0)) == cf.CONV_ERR_NONPOSITIVE
+    assert call(W(groups=4)) == cf.CONV_ERR_SHAPE                  # 4 does not divide 6
+    assert call(W(dilation=5)) == cf.CONV_ERR_SHAPE                # window spans 11 > 8
+    assert call(W(dilation=5, padding=2)) != cf.CONV_ERR_SHAPE     # 8 + 4 >= 11: one output
+    # Y overlapping F: F holds KH*KW*(Cin/groups)*Cout floats.
+    F_end = FA + 3 * 3 * 2 * 6 * 4
+    st = lib.conv2d_nhwc_fwd_window(XA, None, FA, None, F_end - 4, None, 1, 8, 8, 6, 3, 3, 6,
+                                    ctypes.byref(W(groups=3)), cf.CONV_F32, cf.CONV_F32, cf.VARIANT_AUTO, None)
+    assert st == cf.CONV_ERR_ALIAS
+    # depthwise: groups must be 1, asymmetric pads accepted
+    dw = lambda win: lib.conv_depthwise_fwd_window(XA, FA, None, YA, 1, 2, 1, 9, 1, 1, 4,
+                                                   ctypes.byref(win) if win is not None else None,
+                                                   cf.CONV_DW_EXACT, cf.VARIANT_AUTO, None)
+    assert dw(None) == cf.CONV_ERR_NULL
+    assert dw(W(groups=2)) == cf.CONV_ERR_UNSUPPORTED
+    assert dw(W(padding=(0, 0, -1, 0))) == cf.CONV_ERR_NONPOSITIVE
+    assert dw(W(padding=(0, 0, 0, 0), dilation=(1, 3))) == cf.CONV_ERR_SHAPE
+
+
+def test_out_size_window(lib):
+    assert cf.out_size_window(5, 3) == 3
+    assert cf.out_size_window(11, 4, 1, 3, 0, 1) == 11           # causal: K-1 before, none after
+    assert cf.out_size_window(11, 4, 1, 6, 0, 2) == 11           # dilated causal
+    assert cf.out_size_window(224, 16, 16, 0, 0, 1) == 14        # patch stem
+    assert cf.out_size_window(7, 3, 2, 1, 0, 1) == 3
+    assert cf.out_size_window(7, 3, 2, 1, 1, 1) == 4
+    assert cf.out_size_window(2, 5, 1, 0, 0, 1) == 0
+    assert cf.out_size_window(5, 3, 1, -1, 0, 1) == 0
+    for n, k, s, p, d in [(56, 5, 2, 2, 1), (112, 3, 2, 1, 1), (7, 5, 1, 2, 1), (9, 3, 2, 4, 3)]:
+        assert cf.out_size_window(n, k, s, p, p, d) == cf.out_size(n, k, s, p, d)
+
+
+def test_window_auto_variants(lib):
+    """A window other than the lecture's goes to the direct kernel; the plain
+    window through the window entry point is routed like conv2d_nhwc_fwd."""
+    W = cf.window
+    q = lambda win, **k: lib.conv2d_nhwc_window_auto_variant(
+        None, XA, k.get("N", 2), k.get("H", 12), k.get("Wd", 12), 64, 3, 3, 64, ctypes.byref(win),
+        cf.CONV_BF16, cf.CONV_BF16)
+    assert q(W()) == lib.conv2d_nhwc_auto_variant(None, XA, 2, 12, 12, 64, 3, 3, 64, cf.CONV_BF16, cf.CONV_BF16)
+    assert q(W(groups=0)) == -1
+    assert q(W(padding=1, dilation=2)) == cf.VARIANT_DIRECT
+    dq = lambda win: lib.conv_depthwise_window_auto_variant(8, 72, 56, 56, 1, 5, 5, ctypes.byref(win))
+    assert dq(W(stride=2, padding=2)) == lib.conv_depthwise_auto_variant(8, 72, 56, 56, 1, 5, 5, 2, 2, 2, 2, 1, 1)
+    assert dq(W(groups=2)) == -1

@@ -1,0 +1,128 @@
+"""The convolution window on the GPU (stride, padding before/after each axis,
+dilation, groups) against the CPU oracle, through the window entry points.
+
+"Convolution Is Wx+b Moving Across a Signal" defines stride, padding and
+dilation per axis (section "Why 1D? Why 2D?"), grouped channel sums (section
+"Find the same sum in CKE's C kernels"), causal and strided Conv1D (section
+"Where this shows up in models I work with") and the patch stem (section
+"Images going in: two ways to make patches"). Padding that differs before
+and after an axis is checked against the oracle run on the input with the
+zero rows and columns written out, which the oracle pins show is the same
+thing (tests/test_oracle_pins.py).
+"""
+import numpy as np
+import pytest
+import torch
+
+import convolution_forward_amd as cf
+import oracle
+import workloads as wl
+from parity import BF16_RMS_REL, F32_MAX_REL, bf16_ulp_distance, bits, max_rel_err, rms_rel_err
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def pads4(padding):
+    if isinstance(padding, int):
+        return padding, padding, padding, padding
+    if len(padding) == 2:
+        return padding[0], padding[0], padding[1], padding[1]
+    return tuple(padding)
+
+
+def dense_ref(X, F, bias, stride, padding, dilation, groups):
+    pt, pb, pl, pr = pads4(padding)
+    Xp = np.pad(X.float().numpy(), ((0, 0), (pt, pb), (pl, pr), (0, 0)))
+    return oracle.conv2d_nhwc(Xp, F.float().numpy(), bias=None if bias is None else bias.numpy(), stride=stride,
+                              dilation=dilation, groups=groups)
+
+
+DENSE = [  # name, (N,H,W,Cin), (KH,KW,Cout), stride, padding, dilation, groups
+    ("same_3x3", (2, 13, 17, 16), (3, 3, 24), 1, 1, 1, 1),
+    ("stride2_pad1", (2, 15, 14, 32), (3, 3, 40), 2, 1, 1, 1),
+    ("asym_pad", (1, 10, 9, 8), (3, 3, 8), (2, 1), (1, 0, 2, 1), 1, 1),
+    ("dilated", (1, 16, 15, 12), (3, 3, 10), 1, 2, (2, 3), 1),
+    ("grouped", (2, 9, 9, 32), (3, 3, 48), 2, 1, 1, 4),
+    ("grouped_1x1", (2, 6, 7, 24), (1, 1, 36), 1, 0, 1, 3),
+    ("patch_stem", (2, 64, 48, 3), (16, 16, 32), 16, 0, 1, 1),
+    ("conv1d_stride2", (1, 1, 300, 80), (1, 3, 64), (1, 2), (0, 1), 1, 1),
+    ("causal_conv1d", (2, 1, 129, 16), (1, 4, 8), 1, (0, 0, 3, 0), 1, 1),
+    ("causal_dilated", (1, 1, 77, 8), (1, 3, 8), 1, (0, 0, 4, 0), (1, 2), 1),
+]
+
+
+@pytest.mark.parametrize("case", DENSE, ids=lambda c: c[0])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_gpu_dense_window(case, dtype):
+    name, (N, H, W, C), (KH, KW, O), stride, padding, dilation, groups = case
+    seed = 9000 + DENSE.index(case)
+    X = wl.random_tensor((N, H, W, C), seed)
+    F = wl.random_tensor((KH, KW, C // groups, O), seed + 1) * (1.0 / (KH * KW * C / groups) ** 0.5)
+    b = wl.random_tensor((O,), seed + 2)
+    if dtype == "bf16":
+        X, F = X.to(torch.bfloat16), F.to(torch.bfloat16)
+    ref = dense_ref(X, F, b, stride, padding, dilation, groups)
+    kw = dict(stride=stride, padding=padding, dilation=dilation, groups=groups)
+    Y = cf.conv2d_nhwc(X.to(DEV), F.to(DEV), bias=b.to(DEV), out_dtype=torch.float32, **kw)
+    torch.cuda.synchronize()
+    assert tuple(Y.shape) == ref.shape
+    if dtype == "f32":
+        assert max_rel_err(Y, ref) <= F32_MAX_REL
+    else:
+        assert rms_rel_err(Y, ref) <= 1e-3
+        Yb = cf.conv2d_nhwc(X.to(DEV), F.to(DEV), bias=b.to(DEV), **kw)
+        torch.cuda.synchronize()
+        assert rms_rel_err(Yb, ref) <= BF16_RMS_REL and bf16_ulp_distance(Yb, ref) <= 1
+    # every variant that accepts the window gives the same contract
+    for v in (cf.VARIANT_DIRECT, cf.VARIANT_TILED):
+        try:
+            Yv = cf.conv2d_nhwc(X.to(DEV), F.to(DEV), bias=b.to(DEV), out_dtype=torch.float32, variant=v, **kw)
+        except cf.ConvArgumentError as e:
+            assert v == cf.VARIANT_TILED and e.status == cf.CONV_ERR_UNSUPPORTED
+            continue
+        torch.cuda.synchronize()
+        assert (max_rel_err(Yv, ref) <= F32_MAX_REL) if dtype == "f32" else (rms_rel_err(Yv, ref) <= 1e-3)
+
+
+DW = [  # name, (N,C,H,W), mult, (KH,KW), stride, padding (t,b,l,r), dilation
+    ("causal_dw_conv1d", (2, 16, 1, 200), 1, (1, 4), 1, (0, 0, 3, 0), 1),
+    ("causal_dw_dilated", (1, 8, 1, 97), 2, (1, 3), 1, (0, 0, 4, 0), (1, 2)),
+    ("same_even_stride2", (2, 12, 28, 28), 1, (3, 3), 2, (0, 1, 0, 1), 1),
+    ("asym_5x5", (1, 6, 19, 22), 1, (5, 5), 1, (2, 1, 0, 3), 1),
+    ("asym_tiled_3x3", (2, 8, 30, 32), 1, (3, 3), 2, (1, 0, 1, 0), 1),
+]
+
+
+@pytest.mark.parametrize("case", DW, ids=lambda c: c[0])
+@pytest.mark.parametrize("mode", ["exact", "fast"])
+def test_gpu_depthwise_window_bitwise(case, mode):
+    name, (N, C, H, W), m, (KH, KW), stride, padding, dilation = case
+    seed = 9500 + DW.index(case)
+    X = wl.random_tensor((N, C, H, W), seed)
+    w = wl.random_tensor((C * m, KH, KW), seed + 1)
+    b = wl.random_tensor((C * m,), seed + 2)
+    pt, pb, pl, pr = padding
+    Xp = np.pad(X.numpy(), ((0, 0), (0, 0), (pt, pb), (pl, pr)))
+    ref = oracle.depthwise_nchw(Xp, w.numpy(), bias=b.numpy(), stride=stride, padding=0, dilation=dilation,
+                                mode=mode)
+    outs = []
+    for v in (cf.VARIANT_AUTO, cf.VARIANT_DIRECT, cf.VARIANT_TILED):
+        try:
+            Y = cf.conv_depthwise(X.to(DEV), w.to(DEV), bias=b.to(DEV), stride=stride, padding=padding,
+                                  dilation=dilation, exact=(mode == "exact"), variant=v)
+        except cf.ConvArgumentError as e:
+            assert v == cf.VARIANT_TILED and e.status == cf.CONV_ERR_UNSUPPORTED
+            continue
+        torch.cuda.synchronize()
+        assert tuple(Y.shape) == ref.shape
+        g, r = bits(Y), bits(ref)
+        if mode == "exact":
+            np.testing.assert_array_equal(g, r)
+        else:
+            gn, rn = np.isnan(Y.cpu().numpy()), np.isnan(ref)
+            np.testing.assert_array_equal(gn, rn)
+            np.testing.assert_array_equal(g[~gn], r[~rn])
+        outs.append(Y)
+    if name == "asym_tiled_3x3":
+        assert cf.depthwise_variant_for((N, C, H, W), (C * m, KH, KW), stride, padding, dilation) == cf.VARIANT_TILED

@@ -437,3 +437,111 @@ def test_depthwise_matches_torch(oracle_mod, case):
     for mode in ("exact", "fast"):
         got = oracle_mod.depthwise_nchw(X, w, bias=b, stride=s, padding=p, dilation=d, mode=mode)
         np.testing.assert_allclose(got, ref, rtol=1e-5, atol=1e-5)
+
+
+# --- the window superset: each property reduces it to the lecture's operator ----
+
+WINDOW_SHAPES = [  # (N, H, W, Cin, KH, KW, Cout)
+    (1, 9, 7, 3, 3, 3, 2), (2, 6, 11, 2, 2, 3, 3), (1, 12, 12, 4, 5, 5, 1),
+]
+
+
+def _int_inputs(shape, seed):
+    N, H, W, C, KH, KW, O = shape
+    X = random_tensor((N, H, W, C), seed, integer_range=4).numpy()
+    F = random_tensor((KH, KW, C, O), seed + 1, integer_range=4).numpy()
+    return X, F
+
+
+@pytest.mark.parametrize("shape", WINDOW_SHAPES)
+def test_padding_is_explicit_zero_rows_and_columns(oracle_mod, shape):
+    """'Convolution Is Wx+b', section 'Why 1D? Why 2D?': padding inserts zeros
+    at the edges. The padded conv equals the unpadded conv of the input with
+    the zero rows and columns written out (numpy's pad), for each of the four
+    sides separately and together. Integer inputs keep the sums exact."""
+    X, F = _int_inputs(shape, 31)
+    for ph, pw in [(1, 0), (0, 2), (2, 1), (3, 3)]:
+        Xp = np.pad(X, ((0, 0), (ph, ph), (pw, pw), (0, 0)))
+        np.testing.assert_array_equal(oracle_mod.conv2d_nhwc(X, F, padding=(ph, pw)),
+                                      oracle_mod.conv2d_nhwc(Xp, F))
+
+
+@pytest.mark.parametrize("shape", WINDOW_SHAPES)
+def test_stride_subsamples_the_unit_stride_output(oracle_mod, shape):
+    """Same section: stride chooses how far the window moves, so the strided
+    output is every s-th row / column of the unit-stride output."""
+    X, F = _int_inputs(shape, 32)
+    full = oracle_mod.conv2d_nhwc(X, F, padding=1)
+    for sh, sw in [(2, 1), (1, 3), (2, 2), (3, 2)]:
+        got = oracle_mod.conv2d_nhwc(X, F, stride=(sh, sw), padding=1)
+        np.testing.assert_array_equal(got, full[:, ::sh, ::sw, :])
+
+
+@pytest.mark.parametrize("shape", WINDOW_SHAPES)
+def test_dilation_spaces_the_taps(oracle_mod, shape):
+    """Same section: dilation spaces the filter's taps apart, the same as a
+    filter of d*(k-1)+1 taps with zeros between the original ones."""
+    X, F = _int_inputs(shape, 33)
+    KH, KW = F.shape[:2]
+    for dh, dw in [(2, 1), (1, 2), (2, 2)]:
+        Fd = np.zeros((dh * (KH - 1) + 1, dw * (KW - 1) + 1) + F.shape[2:], dtype=np.float32)
+        Fd[::dh, ::dw] = F
+        if Fd.shape[0] > X.shape[1] + 2 or Fd.shape[1] > X.shape[2] + 2:
+            continue
+        np.testing.assert_array_equal(oracle_mod.conv2d_nhwc(X, F, padding=1, dilation=(dh, dw)),
+                                      oracle_mod.conv2d_nhwc(X, Fd, padding=1))
+
+
+@pytest.mark.parametrize("groups", [2, 3, 6])
+def test_groups_are_independent_dense_convs(oracle_mod, groups):
+    """'Convolution Is Wx+b', section 'Find the same sum in CKE's C kernels':
+    an output channel sums over its own group of input channels only. So the
+    grouped conv is the concatenation of one dense conv per group, each on its
+    slice of input channels and output channels."""
+    N, H, W, C, K, O = 2, 7, 8, 6, 3, 12
+    X = random_tensor((N, H, W, C), 34, integer_range=4).numpy()
+    F = random_tensor((K, K, C // groups, O), 35, integer_range=4).numpy()
+    got = oracle_mod.conv2d_nhwc(X, F, stride=2, padding=1, groups=groups)
+    cg, og = C // groups, O // groups
+    parts = [oracle_mod.conv2d_nhwc(np.ascontiguousarray(X[..., g * cg:(g + 1) * cg]),
+                                    np.ascontiguousarray(F[..., g * og:(g + 1) * og]), stride=2, padding=1)
+             for g in range(groups)]
+    np.testing.assert_array_equal(got, np.concatenate(parts, axis=-1))
+
+
+@pytest.mark.parametrize("P", [2, 4, 7])
+def test_patch_stem_is_a_linear_map_of_flattened_patches(oracle_mod, P):
+    """'Convolution Is Wx+b', section 'Images going in: two ways to make
+    patches': a conv with a P x P kernel and stride P over non-overlapping
+    patches equals flattening each patch (row, column, channel) and applying
+    the [P*P*Cin, D] weight matrix."""
+    N, Hp, Wp, C, D = 2, 3, 4, 3, 5
+    X = random_tensor((N, Hp * P, Wp * P, C), 36).numpy()
+    F = random_tensor((P, P, C, D), 37).numpy()
+    got = oracle_mod.conv2d_nhwc(X, F, stride=P)
+    patches = X.reshape(N, Hp, P, Wp, P, C).transpose(0, 1, 3, 2, 4, 5).reshape(N, Hp, Wp, P * P * C)
+    ref = patches.astype(np.float64) @ F.reshape(P * P * C, D).astype(np.float64)
+    np.testing.assert_allclose(got, ref, rtol=1e-13, atol=1e-13)
+
+
+def test_causal_conv1d_is_left_padding(oracle_mod):
+    """'Convolution Is Wx+b', section 'Where this shows up in models I work
+    with' (causal Conv1D): output t sees inputs t-(K-1)*d .. t only. With the
+    signal on the width axis that is K-1 (times dilation) zero columns before
+    it and none after, and the first L outputs of the symmetric padding."""
+    L, C, K, O, d = 11, 3, 4, 2, 2
+    X = random_tensor((1, 1, L, C), 38, integer_range=4).numpy()
+    F = random_tensor((1, K, C, O), 39, integer_range=4).numpy()
+    pad = d * (K - 1)
+    left = oracle_mod.conv2d_nhwc(np.pad(X, ((0, 0), (0, 0), (pad, 0), (0, 0))), F, dilation=(1, d))
+    assert left.shape == (1, 1, L, O)
+    sym = oracle_mod.conv2d_nhwc(X, F, padding=(0, pad), dilation=(1, d))
+    np.testing.assert_array_equal(left, sym[:, :, :L, :])
+    # brute force of the causal definition
+    ref = np.zeros((L, O))
+    for t in range(L):
+        for k in range(K):
+            src = t - (K - 1 - k) * d
+            if src >= 0:
+                ref[t] += X[0, 0, src].astype(np.float64) @ F[0, k].astype(np.float64)
+    np.testing.assert_array_equal(left[0, 0], ref)
