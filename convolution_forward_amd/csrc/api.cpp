@@ -159,9 +159,9 @@ conv_status validate_dense(const void *X, const int64_t *x_strides, const void *
 // The tiled (matrix-core) variant: one kernel family per operand type.
 bool dense_tiled_supports(const DenseProblem &p)
 {
-    if (!plain_window(p))
-        return false;
-    return p.xdt == CONV_BF16 ? dense_mfma_bf16_supports(p) : dense_mfma_f32_supports(p);
+    if (p.xdt == CONV_BF16)
+        return dense_mfma_bf16_supports(p);
+    return plain_window(p) && dense_mfma_f32_supports(p);
 }
 
 hipError_t launch_dense_tiled(const DenseProblem &p, hipStream_t s)

@@ -69,39 +69,54 @@ struct RowArgs {
     const float *bias;
     void *Y;
     int64_t xs0, xs1, xs2, ys0, ys1, ys2;
-    int H, W, Cin, Cout, Ho, Wo;
+    int H, W, Ho, Wo;
+    int Cin, Cout;      // channels of one group (input, output)
+    int f_ld;           // F row length: output channels of all groups
+    int pt, pl;         // zero rows / columns before the input
     int R;              // output rows per band
     int bands_per_img;
     int bands;          // N * bands_per_img (the grid may hold more: those exit)
-    int tiles;          // 64-channel output tiles
-    int row_elems;      // LDS elements per staged input row (W * pitch)
-    int chunks_per_row; // 16-byte chunks per staged input row (W * Cin_padded / 8)
+    int tiles;          // 64-channel output tiles per group
+    int groups;
+    int row_slots;      // pixel slots of a staged input row (zero padding included)
+    int row_elems;      // LDS elements per staged input row (row_slots * pitch)
+    int chunks_per_row; // 16-byte chunks of real input per row (W * Cin_padded / 8)
     int otile_off;      // LDS byte offset of the output tiles
     uint32_t x_records; // bytes addressable from one image's base in X
     uint32_t y_records; // bytes addressable from one image's base in Y
 };
 
-// Byte offset of 16-byte chunk q (pixel q / CG, channel group q % CG) of
-// input row r inside the image, or OOB when the chunk is padding or outside
-// the band: the buffer load then returns zeros without touching memory.
+// LDS pixel pitch of a staged row, in bf16 elements. Lanes read pixels S
+// slots apart, and 16-byte reads of 16 lanes are conflict-free when the lane
+// step is 32 modulo 64 bytes: Cin_padded + 16 for S = 1 (CINP*2 + 32 bytes),
+// Cin_padded + 8 for S = 2 (twice CINP*2 + 16 bytes).
+template <int CINP, int S>
+constexpr int row_pitch() { return S == 1 ? CINP + 16 : CINP + 8; }
+
+// Byte offset (from the image's base) of 16-byte chunk q (pixel q / CG,
+// channel group q % CG) of input row iy, or OOB when the chunk is padding,
+// outside the image or past the rows the band reads: the buffer load then
+// returns zeros without touching memory.
 template <int CINP>
-__device__ __forceinline__ uint32_t chunk_off(const RowArgs &a, int r, int q, int rows_end)
+__device__ __forceinline__ uint32_t chunk_off(const RowArgs &a, int iy, int q, int iy_end)
 {
     constexpr int CG = CINP / 8;
     const int px = q / CG;
     const int cg = q - px * CG;
-    const bool ok = q < a.chunks_per_row && r < rows_end && cg * 8 < a.Cin;
-    return ok ? (uint32_t)(((int64_t)r * a.xs1 + (int64_t)px * a.xs2 + cg * 8) * 2) : OOB;
+    const bool ok = q < a.chunks_per_row && iy >= 0 && iy < iy_end && cg * 8 < a.Cin;
+    return ok ? (uint32_t)(((int64_t)iy * a.xs1 + (int64_t)px * a.xs2 + cg * 8) * 2) : OOB;
 }
 
-template <int CINP>
-__device__ __forceinline__ void put_chunk(uint16_t *lds_row, int q, u32x4 v)
+// Chunk q of a row lands in pixel slot (q / CG) + pl: the first pl slots and
+// those past the input hold the zero padding.
+template <int CINP, int S>
+__device__ __forceinline__ void put_chunk(uint16_t *lds_row, int pl, int q, u32x4 v)
 {
     constexpr int CG = CINP / 8;
-    constexpr int PITCH = CINP + 16;
+    constexpr int PITCH = row_pitch<CINP, S>();
     const int px = q / CG;
     const int cg = q - px * CG;
-    *reinterpret_cast<u32x4 *>(lds_row + px * PITCH + cg * 8) = v;
+    *reinterpret_cast<u32x4 *>(lds_row + (px + pl) * PITCH + cg * 8) = v;
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
@@ -138,10 +153,12 @@ struct FilterSlice {
 
     u32x4 fv[ITEMS];
 
-    __device__ __forceinline__ void issue(const RowArgs &a, int o0, int tid)
+    // o0: first output channel of the tile within its group; oc0: first
+    // output channel of the group (F rows hold all groups' outputs).
+    __device__ __forceinline__ void issue(const RowArgs &a, int o0, int oc0, int tid)
     {
         const __amdgpu_buffer_rsrc_t fr = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint16_t *>(a.F), 0, KH * KW * a.Cin * a.Cout * 2, BUF_WORD3);
+            const_cast<uint16_t *>(a.F), 0, KH * KW * a.Cin * a.f_ld * 2, BUF_WORD3);
 #pragma unroll
         for (int t = 0; t < ITEMS; ++t) {
             const int it = tid + t * THREADS;
@@ -151,7 +168,7 @@ struct FilterSlice {
             const int o = o0 + og * 8;
             const bool ok = tap < KH * KW && c < a.Cin && o < a.Cout;
             fv[t] = __builtin_amdgcn_raw_buffer_load_b128(
-                fr, ok ? (uint32_t)((((int64_t)tap * a.Cin + c) * a.Cout + o) * 2) : OOB, 0, 0);
+                fr, ok ? (uint32_t)((((int64_t)tap * a.Cin + c) * a.f_ld + oc0 + o) * 2) : OOB, 0, 0);
         }
     }
 
@@ -203,24 +220,37 @@ struct FilterSlice {
 
 // Bias of the 4 output channels of each column block a lane's results
 // belong to (zeros without bias).
-__device__ __forceinline__ void bias_issue(const RowArgs &a, int o0, int half, int lane, u32x4 (&bq)[NBW])
+__device__ __forceinline__ void bias_issue(const RowArgs &a, int o0, int oc0, int half, int lane, u32x4 (&bq)[NBW])
 {
     const __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc(
-        a.bias ? (void *)a.bias : (void *)a.F, 0, a.bias ? a.Cout * 4 : 0, BUF_WORD3);
+        a.bias ? (void *)(a.bias + oc0) : (void *)a.F, 0, a.bias ? a.Cout * 4 : 0, BUF_WORD3);
 #pragma unroll
     for (int nb = 0; nb < NBW; ++nb)
         bq[nb] = __builtin_amdgcn_raw_buffer_load_b128(
             br, (uint32_t)((o0 + half * 32 + nb * 16 + (lane >> 4) * 4) * 4), 0, 0);
 }
 
-template <int KH, int KW, int CS, int BPW, int MAXC, int NR, bool OUT_BF16>
+// S is the stride along both axes (1 or 2). A band of output rows
+// t = 0..R-1 reads input rows y0*S - pt + r for r = 0..(R-1)*S + KH - 1;
+// output row t uses rows r = t*S + i (filter row i). NR bounds that count.
+template <int KH, int KW, int S>
+struct Window {
+    static constexpr int INFLIGHT = (KH + S - 1) / S;    // output rows summing at once
+    // Output row t of a band of at most RMAX rows completes at step t*S + KH - 1.
+    static constexpr bool completes(int r, int RMAX) { return r >= KH - 1 && (r - (KH - 1)) % S == 0 && (r - (KH - 1)) / S < RMAX; }
+};
+
+template <int KH, int KW, int CS, int BPW, int MAXC, int NR, int S, bool OUT_BF16>
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void dense_rows_mfma(RowArgs a)
 {
     constexpr int CINP = 32 * CS;
-    constexpr int PITCH = CINP + 16;
+    constexpr int PITCH = row_pitch<CINP, S>();
+    constexpr int CG = CINP / 8;
     constexpr int KSTEPS = KH * KW * CS;
     constexpr int ESZ = OUT_BF16 ? 2 : 4;
+    constexpr int RMAX = (NR - KH) / S + 1;          // output rows a band can hold
+    constexpr int T = Window<KH, KW, S>::INFLIGHT;
     // Output tile: one row of results (64 pixels per block slot x 64
     // channels), double buffered, padded to a pitch of 32 mod 64 bytes.
     constexpr int OPITCH = COUT_TILE * ESZ + 32;
@@ -248,9 +278,14 @@ void dense_rows_mfma(RowArgs a)
     // tile (s/8) % tiles. All tiles of a band and consecutive bands of one
     // image then run on one XCD, so the input rows they share (the whole band
     // across tiles, the halo rows across bands) meet in that XCD's L2.
+    const int tiles_all = a.tiles * a.groups;
     const int slot_in_xcd = (int)(blockIdx.x >> 3);
-    const int band = (int)(blockIdx.x & 7) * (int)(gridDim.x >> 3) / a.tiles + slot_in_xcd / a.tiles;
-    const int o0 = (slot_in_xcd % a.tiles) * COUT_TILE;
+    const int band = (int)(blockIdx.x & 7) * (int)(gridDim.x >> 3) / tiles_all + slot_in_xcd / tiles_all;
+    const int tile = slot_in_xcd % tiles_all;
+    const int grp = tile / a.tiles;
+    const int o0 = (tile - grp * a.tiles) * COUT_TILE;   // within the group
+    const int xc0 = grp * a.Cin;                          // group's first input channel
+    const int oc0 = grp * a.Cout;                         // group's first output channel
     if (band >= a.bands)
         return;
     const int n = band / a.bands_per_img;
@@ -258,18 +293,19 @@ void dense_rows_mfma(RowArgs a)
     if (y0 >= a.Ho)
         return;
     const int y1 = min(y0 + a.R, a.Ho);
-    const int rows_end = y1 + KH - 1;           // one past the last input row this band reads
+    const int iy0 = y0 * S - a.pt;                        // input row of step 0
+    const int iy_end = min(a.H, (y1 - 1) * S - a.pt + KH);  // one past the last input row the band reads
 
     const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t *>(a.X + (int64_t)n * a.xs0), 0, (int)a.x_records, BUF_WORD3);
+        const_cast<uint16_t *>(a.X + (int64_t)n * a.xs0 + xc0), 0, (int)(a.x_records - xc0 * 2), BUF_WORD3);
     const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(
-        static_cast<char *>(a.Y) + (int64_t)n * a.ys0 * ESZ, 0, (int)a.y_records, BUF_WORD3);
+        static_cast<char *>(a.Y) + ((int64_t)n * a.ys0 + oc0) * ESZ, 0, (int)(a.y_records - oc0 * ESZ), BUF_WORD3);
 
     // 1. Filter slice and bias first.
     FilterSlice<KH, KW, CS> filt;
-    filt.issue(a, o0, tid);
+    filt.issue(a, o0, oc0, tid);
     u32x4 bq[NBW];
-    bias_issue(a, o0, half, lane, bq);
+    bias_issue(a, o0, oc0, half, lane, bq);
 
     // 2. The first D input rows of the band; the loop below keeps loading D
     //    rows ahead of use. The fence keeps the scheduler from hoisting these
@@ -284,7 +320,7 @@ void dense_rows_mfma(RowArgs a)
 #pragma unroll
         for (int k = 0; k < MAXC; ++k)
             xin[i][k] = __builtin_amdgcn_raw_buffer_load_b128(
-                xr, chunk_off<CINP>(a, y0 + i, tid + k * THREADS, rows_end), 0, 0);
+                xr, chunk_off<CINP>(a, iy0 + i, tid + k * THREADS, iy_end), 0, 0);
 
     // 3. Filter slice into LDS, then 4. its A fragments into registers.
     filt.commit(ft, tid);
@@ -293,12 +329,23 @@ void dense_rows_mfma(RowArgs a)
     FilterSlice<KH, KW, CS>::fragments(ft, lane, half, wf);
     __syncthreads();      // the staging area becomes the input-row area
 
-    // 5. Input row 0 into LDS.
+    // 5. Zero the padding slots of both row buffers (never overwritten
+    //    afterwards), and input row 0 into buffer 0.
+    {
+        const int zslots = a.row_slots - a.W;
+        for (int q = tid; q < 2 * zslots * CG; q += THREADS) {
+            const int b = q / (zslots * CG);
+            const int zq = q - b * zslots * CG;
+            const int zi = zq / CG;
+            const int slot = zi < a.pl ? zi : zi + a.W;
+            *reinterpret_cast<u32x4 *>(rows + b * a.row_elems + slot * PITCH + (zq - zi * CG) * 8) = u32x4{0, 0, 0, 0};
+        }
+    }
 #pragma unroll
     for (int k = 0; k < MAXC; ++k) {
         const int q = tid + k * THREADS;
         if (q < a.chunks_per_row)
-            put_chunk<CINP>(rows, q, xin[0][k]);
+            put_chunk<CINP, S>(rows, a.pl, q, xin[0][k]);
     }
     __syncthreads();
 
@@ -323,18 +370,19 @@ void dense_rows_mfma(RowArgs a)
     };
 
     // 6. Slide down the band one input row at a time. Input row r feeds
-    //    output rows t = r - i for filter rows i = 0..KH-1, so each X fragment
-    //    read from LDS serves up to KH output rows: KW*CS fragments per input
-    //    row instead of KH*KW*CS per output row. Output row t accumulates in
-    //    slot t % KH during steps t .. t+KH-1 (taps in ascending i, then j,
-    //    then channel step); at step t+KH-1 it is complete, goes to output
-    //    tile t & 1, and leaves at step t+KH after the barrier.
+    //    output rows t = (r - i) / S for the filter rows i with r - i a
+    //    multiple of S, so each X fragment read from LDS serves every output
+    //    row that uses that input row. Output row t accumulates in slot t % T
+    //    (taps in ascending i, then j, then channel step); it is complete at
+    //    step t*S + KH - 1, goes to output tile t & 1, and leaves at the next
+    //    step, after the barrier.
     //    The loop is fully unrolled (NR steps, all indices static) and every
     //    global operation in it is unconditional, so the waits the compiler
     //    places for prefetched rows never include the stores.
-    f32x4 acc[KH][BPW][NBW];
+    using Win = Window<KH, KW, S>;
+    f32x4 acc[T][BPW][NBW];
 #pragma unroll
-    for (int s2 = 0; s2 < KH; ++s2)
+    for (int s2 = 0; s2 < T; ++s2)
 #pragma unroll
         for (int qb = 0; qb < BPW; ++qb)
 #pragma unroll
@@ -343,13 +391,13 @@ void dense_rows_mfma(RowArgs a)
 
     static_for<0, NR>([&](auto RR) {
         constexpr int r = decltype(RR)::value;
-        if constexpr (r >= KH)
-            store_row(r - KH);
+        if constexpr (r >= 1 && Win::completes(r - 1, RMAX))
+            store_row((r - KH) / S);
         if constexpr (r + D < NR) {
 #pragma unroll
             for (int k = 0; k < MAXC; ++k)
                 xin[(r + D) % D][k] = __builtin_amdgcn_raw_buffer_load_b128(
-                    xr, chunk_off<CINP>(a, y0 + r + D, tid + k * THREADS, rows_end), 0, 0);
+                    xr, chunk_off<CINP>(a, iy0 + r + D, tid + k * THREADS, iy_end), 0, 0);
         }
         const uint16_t *rowp = rows + (r & 1) * a.row_elems;
 #pragma unroll
@@ -361,31 +409,32 @@ void dense_rows_mfma(RowArgs a)
             for (int jc = 0; jc < KW * CS; ++jc) {
                 const int j = jc / CS;
                 const int cs = jc % CS;
-                xb[jc] = *reinterpret_cast<const bf16x8 *>(rowp + (xl + j) * PITCH + cs * 32 + (lane >> 4) * 8);
+                xb[jc] = *reinterpret_cast<const bf16x8 *>(rowp + (xl * S + j) * PITCH + cs * 32 + (lane >> 4) * 8);
             }
 #pragma unroll
             for (int i = 0; i < KH; ++i) {
-                const int t = r - i;                     // output row fed by filter row i
-                if (t >= 0 && t <= NR - KH && y0 + t < y1) {
+                const int d = r - i;                      // t * S for the output row this tap feeds
+                const int t = d / S;
+                if (d >= 0 && d % S == 0 && t < RMAX && y0 + t < y1) {
 #pragma unroll
                     for (int jc = 0; jc < KW * CS; ++jc) {
                         const int ks = i * KW * CS + jc;
 #pragma unroll
                         for (int nb = 0; nb < NBW; ++nb)
-                            acc[(t + KH) % KH][qb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                wf[ks][nb], xb[jc], acc[(t + KH) % KH][qb][nb], 0, 0, 0);
+                            acc[t % T][qb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                wf[ks][nb], xb[jc], acc[t % T][qb][nb], 0, 0, 0);
                     }
                 }
             }
-            if constexpr (r >= KH - 1) {
-                // Output row t = r - KH + 1 is complete: lane holds channels
+            if constexpr (Win::completes(r, RMAX)) {
+                // Output row t is complete: lane holds channels
                 // 32*half+16nb+4*(lane/16)+{0..3} of pixel x.
-                constexpr int t = r - KH + 1;
+                constexpr int t = (r - (KH - 1)) / S;
                 uint8_t *orow = otile + (t & 1) * OTILE_BYTES + x * OPITCH;
 #pragma unroll
                 for (int nb = 0; nb < NBW; ++nb) {
                     const int cl = half * 32 + nb * 16 + (lane >> 4) * 4;
-                    const f32x4 v = acc[t % KH][qb][nb];
+                    const f32x4 v = acc[t % T][qb][nb];
                     const float v0 = v[0] + __uint_as_float(bq[nb][0]);
                     const float v1 = v[1] + __uint_as_float(bq[nb][1]);
                     const float v2 = v[2] + __uint_as_float(bq[nb][2]);
@@ -396,7 +445,7 @@ void dense_rows_mfma(RowArgs a)
                         *reinterpret_cast<u32x4 *>(orow + cl * 4) =
                             u32x4{__float_as_uint(v0), __float_as_uint(v1), __float_as_uint(v2), __float_as_uint(v3)};
                     }
-                    acc[t % KH][qb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    acc[t % T][qb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
                 }
             }
         }
@@ -409,12 +458,13 @@ void dense_rows_mfma(RowArgs a)
             for (int k = 0; k < MAXC; ++k) {
                 const int q = tid + k * THREADS;
                 if (q < a.chunks_per_row)
-                    put_chunk<CINP>(rows + ((r + 1) & 1) * a.row_elems, q, xin[(r + 1) % D][k]);
+                    put_chunk<CINP, S>(rows + ((r + 1) & 1) * a.row_elems, a.pl, q, xin[(r + 1) % D][k]);
             }
         }
         __syncthreads();
     });
-    store_row(NR - KH);
+    if constexpr (Win::completes(NR - 1, RMAX))
+        store_row((NR - KH) / S);
 }
 
 // --- host side -------------------------------------------------------------
@@ -428,12 +478,12 @@ int cin_steps(int Cin)
     return 0;
 }
 
-bool taps_instantiated(int KH, int KW, int CS)
+bool taps_instantiated(int KH, int KW, int CS, int S)
 {
     if (KH == 1 && KW == 1)
-        return CS == 1 || CS == 2 || CS == 4 || CS == 8 || CS == 16;
+        return S == 1 ? (CS == 1 || CS == 2 || CS == 4 || CS == 8 || CS == 16) : (CS == 1 || CS == 2 || CS == 4 || CS == 8);
     if (KH == 2 && KW == 2)
-        return CS == 1 || CS == 2 || CS == 4;
+        return S == 1 && (CS == 1 || CS == 2 || CS == 4);
     if (KH == 3 && KW == 3)
         return CS == 1 || CS == 2;
     return false;
@@ -444,8 +494,16 @@ bool taps_instantiated(int KH, int KW, int CS)
 // by registers or LDS.
 constexpr int rows_in_regs(int MAXC) { return MAXC == 1 ? 9 : MAXC == 2 ? 9 : 13; }
 
+// Loads per thread for one input row, at most, for rows that fit the
+// kernel (64 * BPW output pixels at stride S, plus the halo).
+constexpr int max_chunks(int KW, int CS, int BPW, int S) { return ((64 * BPW * S + KW - 1) * 4 * CS + THREADS - 1) / THREADS; }
+
+// Four chunks per thread are instantiated only for 1x1 filters: with a
+// larger window the row registers no longer fit beside the filter.
+constexpr bool wide_rows_ok(int KH) { return KH == 1; }
+
 struct Plan {
-    int CS, BPW, MAXC, NR, R;
+    int S, CS, BPW, MAXC, NR, R, slots;
     size_t otile_off, lds;
 };
 
@@ -455,21 +513,27 @@ int64_t image_extent(const int64_t *s, int rows, int cols, int ch, int esz)
     return ((int64_t)(rows - 1) * s[1] + (int64_t)(cols - 1) * s[2] + ch) * esz;
 }
 
-// Loads per thread for one input row, at most, for rows that fit the
-// kernel (64 * BPW output pixels plus the halo).
-constexpr int max_chunks(int KW, int CS, int BPW) { return ((64 * BPW + KW - 1) * 4 * CS + THREADS - 1) / THREADS; }
-
-// Four chunks per thread are instantiated only for 1x1 filters: with a
-// larger window the row registers no longer fit beside the filter.
-constexpr bool wide_rows_ok(int KH) { return KH == 1; }
+// The stride the kernel runs with (1 or 2, the same on both axes, no
+// dilation), or 0 when the window needs the direct kernel.
+int kernel_stride(const DenseProblem &p)
+{
+    if (p.sh != p.sw || (p.sh != 1 && p.sh != 2) || p.dh != 1 || p.dw != 1)
+        return 0;
+    return p.sh;
+}
 
 bool plan_rows(const DenseProblem &p, Plan *plan)
 {
-    if (p.xdt != CONV_BF16 || p.Cin % 8 != 0 || p.Cout % 8 != 0)
+    Plan pl;
+    pl.S = kernel_stride(p);
+    if (pl.S == 0 || p.xdt != CONV_BF16)
+        return false;
+    const int cin_g = p.Cin / p.groups, cout_g = p.Cout / p.groups;
+    if (cin_g % 8 != 0 || cout_g % 8 != 0)
         return false;
     if ((uintptr_t)p.X % 16 != 0 || p.xs[0] % 8 != 0 || p.xs[1] % 8 != 0 || p.xs[2] % 8 != 0)
         return false;
-    if ((uintptr_t)p.F % 16 != 0 || (int64_t)p.KH * p.KW * p.Cin * p.Cout * 2 >= (int64_t(1) << 31))
+    if ((uintptr_t)p.F % 16 != 0 || (int64_t)p.KH * p.KW * cin_g * p.Cout * 2 >= (int64_t(1) << 31))
         return false;
     // Output rows leave in 16-byte chunks of 8 (bf16) or 4 (fp32) channels.
     const int yesz = p.ydt == CONV_BF16 ? 2 : 4;
@@ -480,9 +544,8 @@ bool plan_rows(const DenseProblem &p, Plan *plan)
     if (image_extent(p.xs, p.H, p.W, p.Cin, 2) >= (int64_t(1) << 31) ||
         image_extent(p.ys, p.Ho, p.Wo, p.Cout, yesz) >= (int64_t(1) << 31))
         return false;
-    Plan pl;
-    pl.CS = cin_steps(p.Cin);
-    if (pl.CS == 0 || !taps_instantiated(p.KH, p.KW, pl.CS))
+    pl.CS = cin_steps(cin_g);
+    if (pl.CS == 0 || !taps_instantiated(p.KH, p.KW, pl.CS, pl.S))
         return false;
     const int blocks = (p.Wo + 15) / 16;
     pl.BPW = (blocks + 3) / 4;
@@ -490,22 +553,25 @@ bool plan_rows(const DenseProblem &p, Plan *plan)
         return false;
     const int64_t chunks = (int64_t)p.W * 32 * pl.CS / 8;
     pl.MAXC = chunks <= THREADS ? 1 : chunks <= 2 * THREADS ? 2 : chunks <= 4 * THREADS ? 4 : 0;
-    if (pl.MAXC == 0 || (pl.MAXC == 4 && !wide_rows_ok(p.KH)))
+    if (pl.MAXC == 0 || (pl.MAXC == 4 && !wide_rows_ok(p.KH)) || pl.MAXC > max_chunks(p.KW, pl.CS, pl.BPW, pl.S))
         return false;
     pl.NR = rows_in_regs(pl.MAXC);
-    const int rmax = pl.NR - p.KH + 1;             // output rows a band can hold
-    if (rmax < 1)
+    if (pl.NR < p.KH)
         return false;
+    const int rmax = (pl.NR - p.KH) / pl.S + 1;      // output rows a band can hold
     // Bands: aim for about one workgroup per compute unit (256) in total.
-    const int tiles = (p.Cout + COUT_TILE - 1) / COUT_TILE;
+    const int tiles = (cout_g + COUT_TILE - 1) / COUT_TILE * p.groups;
     int want = (int)((256 + (int64_t)p.N * tiles - 1) / ((int64_t)p.N * tiles));
     want = want < 1 ? 1 : want > p.Ho ? p.Ho : want;
     const int R = (p.Ho + want - 1) / want;
     pl.R = R < rmax ? R : rmax;
+    // A staged row holds the pixels the outputs read and every real pixel.
+    const int need = (p.Wo - 1) * pl.S + p.KW;
+    pl.slots = need > p.pl + p.W ? need : p.pl + p.W;
     // LDS: [max(filter staging, two input rows)] [two output tiles].
-    const size_t pitch = (size_t)32 * pl.CS + 16;
+    const size_t pitch = pl.S == 1 ? (size_t)32 * pl.CS + 16 : (size_t)32 * pl.CS + 8;
     const size_t filt = (size_t)p.KH * p.KW * 32 * pl.CS * (COUT_TILE + 8) * 2;
-    const size_t rows = (size_t)2 * p.W * pitch * 2;
+    const size_t rows = (size_t)2 * pl.slots * pitch * 2;
     pl.otile_off = filt > rows ? filt : rows;
     pl.lds = pl.otile_off + 2 * (size_t)64 * pl.BPW * (COUT_TILE * yesz + 32);
     if (pl.lds > (size_t)LDS_BYTES_MAX)
@@ -514,14 +580,14 @@ bool plan_rows(const DenseProblem &p, Plan *plan)
     return true;
 }
 
-template <int KH, int KW, int CS, int BPW, int MAXC, bool OB>
+template <int KH, int KW, int CS, int BPW, int MAXC, int S, bool OB>
 hipError_t launch_inst(const RowArgs &a, dim3 grid, size_t lds, hipStream_t s)
 {
     constexpr int NR = rows_in_regs(MAXC);
-    if constexpr (NR - KH + 1 < 1) {
+    if constexpr (NR < KH) {
         return hipErrorNotSupported;
     } else {
-        auto kern = dense_rows_mfma<KH, KW, CS, BPW, MAXC, NR, OB>;
+        auto kern = dense_rows_mfma<KH, KW, CS, BPW, MAXC, NR, S, OB>;
         // Allow the full LDS once per instantiation (first launch, before any
         // graph capture a caller may start later).
         static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
@@ -533,19 +599,19 @@ hipError_t launch_inst(const RowArgs &a, dim3 grid, size_t lds, hipStream_t s)
     }
 }
 
-template <int KH, int KW, int CS, int BPW>
+template <int KH, int KW, int CS, int BPW, int S>
 hipError_t launch_bpw(const RowArgs &a, dim3 grid, size_t lds, int MAXC, bool ob, hipStream_t s)
 {
-    constexpr int CMAX = max_chunks(KW, CS, BPW);
+    constexpr int CMAX = max_chunks(KW, CS, BPW, S);
     if (MAXC == 1)
-        return ob ? launch_inst<KH, KW, CS, BPW, 1, true>(a, grid, lds, s) : launch_inst<KH, KW, CS, BPW, 1, false>(a, grid, lds, s);
+        return ob ? launch_inst<KH, KW, CS, BPW, 1, S, true>(a, grid, lds, s) : launch_inst<KH, KW, CS, BPW, 1, S, false>(a, grid, lds, s);
     if constexpr (CMAX >= 2) {
         if (MAXC == 2)
-            return ob ? launch_inst<KH, KW, CS, BPW, 2, true>(a, grid, lds, s) : launch_inst<KH, KW, CS, BPW, 2, false>(a, grid, lds, s);
+            return ob ? launch_inst<KH, KW, CS, BPW, 2, S, true>(a, grid, lds, s) : launch_inst<KH, KW, CS, BPW, 2, S, false>(a, grid, lds, s);
     }
     if constexpr (CMAX >= 3 && wide_rows_ok(KH)) {
         if (MAXC == 4)
-            return ob ? launch_inst<KH, KW, CS, BPW, 4, true>(a, grid, lds, s) : launch_inst<KH, KW, CS, BPW, 4, false>(a, grid, lds, s);
+            return ob ? launch_inst<KH, KW, CS, BPW, 4, S, true>(a, grid, lds, s) : launch_inst<KH, KW, CS, BPW, 4, S, false>(a, grid, lds, s);
     }
     return hipErrorNotSupported;
 }
@@ -553,20 +619,23 @@ hipError_t launch_bpw(const RowArgs &a, dim3 grid, size_t lds, int MAXC, bool ob
 template <int KH, int KW, int CS>
 hipError_t launch_cs(const RowArgs &a, dim3 grid, const Plan &plan, bool ob, hipStream_t s)
 {
-    if (plan.BPW == 1)
-        return launch_bpw<KH, KW, CS, 1>(a, grid, plan.lds, plan.MAXC, ob, s);
-    return launch_bpw<KH, KW, CS, 2>(a, grid, plan.lds, plan.MAXC, ob, s);
+    if (plan.S == 1)
+        return plan.BPW == 1 ? launch_bpw<KH, KW, CS, 1, 1>(a, grid, plan.lds, plan.MAXC, ob, s)
+                             : launch_bpw<KH, KW, CS, 2, 1>(a, grid, plan.lds, plan.MAXC, ob, s);
+    if constexpr ((KH == 3 && CS <= 2) || (KH == 1 && CS <= 8))
+        return plan.BPW == 1 ? launch_bpw<KH, KW, CS, 1, 2>(a, grid, plan.lds, plan.MAXC, ob, s)
+                             : launch_bpw<KH, KW, CS, 2, 2>(a, grid, plan.lds, plan.MAXC, ob, s);
+    return hipErrorNotSupported;
 }
-
-}  // namespace
 
 // A 1x1 filter makes every pixel independent: when the pixels of X and Y
 // sit at one pixel stride (within each image, or across the whole batch),
 // regroup them into rows of 64 (or another width that divides the pixel
-// count) so no 16-pixel block of a row is left partly empty.
+// count) so no 16-pixel block of a row is left partly empty. Only for the
+// plain window: padding and stride tie outputs to input positions.
 DenseProblem regroup_pointwise(const DenseProblem &p)
 {
-    if (p.KH != 1 || p.KW != 1)
+    if (p.KH != 1 || p.KW != 1 || !plain_window(p))
         return p;
     if (p.xs[1] != (int64_t)p.W * p.xs[2] || p.ys[1] != (int64_t)p.Wo * p.ys[2])
         return p;
@@ -608,6 +677,8 @@ DenseProblem regroup_pointwise(const DenseProblem &p)
     return q;
 }
 
+}  // namespace
+
 bool dense_mfma_bf16_supports(const DenseProblem &p)
 {
     Plan plan;
@@ -633,11 +704,16 @@ hipError_t launch_dense_mfma_bf16(const DenseProblem &p0, hipStream_t s)
     a.ys2 = p.ys[2];
     a.H = p.H;
     a.W = p.W;
-    a.Cin = p.Cin;
-    a.Cout = p.Cout;
     a.Ho = p.Ho;
     a.Wo = p.Wo;
-    a.row_elems = p.W * (32 * plan.CS + 16);
+    a.Cin = p.Cin / p.groups;
+    a.Cout = p.Cout / p.groups;
+    a.f_ld = p.Cout;
+    a.pt = p.pt;
+    a.pl = p.pl;
+    a.groups = p.groups;
+    a.row_slots = plan.slots;
+    a.row_elems = plan.slots * (plan.S == 1 ? 32 * plan.CS + 16 : 32 * plan.CS + 8);
     a.chunks_per_row = p.W * 32 * plan.CS / 8;
     a.otile_off = (int)plan.otile_off;
     a.x_records = (uint32_t)image_extent(p.xs, p.H, p.W, p.Cin, 2);
@@ -645,10 +721,10 @@ hipError_t launch_dense_mfma_bf16(const DenseProblem &p0, hipStream_t s)
     a.R = plan.R;
     a.bands_per_img = (p.Ho + a.R - 1) / a.R;
     a.bands = p.N * a.bands_per_img;
-    a.tiles = (p.Cout + COUT_TILE - 1) / COUT_TILE;
-    // One slot per (band, tile), bands padded to a multiple of 8 (the
+    a.tiles = (a.Cout + COUT_TILE - 1) / COUT_TILE;
+    // One slot per (band, group, tile), bands padded to a multiple of 8 (the
     // padding slots exit at once) for the XCD-aware slot map.
-    const int64_t slots = (int64_t)((a.bands + 7) / 8 * 8) * a.tiles;
+    const int64_t slots = (int64_t)((a.bands + 7) / 8 * 8) * a.tiles * a.groups;
     if (slots >= (int64_t(1) << 31))
         return hipErrorNotSupported;
     const dim3 grid((unsigned)slots);

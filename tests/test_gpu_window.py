@@ -49,6 +49,15 @@ DENSE = [  # name, (N,H,W,Cin), (KH,KW,Cout), stride, padding, dilation, groups
     ("conv1d_stride2", (1, 1, 300, 80), (1, 3, 64), (1, 2), (0, 1), 1, 1),
     ("causal_conv1d", (2, 1, 129, 16), (1, 4, 8), 1, (0, 0, 3, 0), 1, 1),
     ("causal_dilated", (1, 1, 77, 8), (1, 3, 8), 1, (0, 0, 4, 0), (1, 2), 1),
+    # windows the bf16 matrix-core kernel takes (padding, stride 2, groups)
+    ("mfma_same_3x3", (2, 20, 30, 64), (3, 3, 64), 1, 1, 1, 1),
+    ("mfma_stride2_3x3", (2, 33, 40, 32), (3, 3, 48), 2, 1, 1, 1),
+    ("mfma_stride2_asym", (1, 28, 28, 16), (3, 3, 16), 2, (0, 1, 0, 1), 1, 1),
+    ("mfma_grouped_3x3", (2, 12, 14, 64), (3, 3, 64), 1, 1, 1, 4),
+    ("mfma_grouped_1x1_s2", (2, 14, 14, 64), (1, 1, 128), 2, 0, 1, 2),
+    ("mfma_1x1_padded", (1, 9, 10, 32), (1, 1, 40), 1, 1, 1, 1),
+    ("mfma_wide_same", (1, 6, 120, 16), (3, 3, 16), 1, 1, 1, 1),
+    ("mfma_pad_2_stride2", (1, 17, 9, 24), (3, 3, 8), 2, 2, 1, 1),
 ]
 
 
@@ -74,6 +83,8 @@ def test_gpu_dense_window(case, dtype):
         Yb = cf.conv2d_nhwc(X.to(DEV), F.to(DEV), bias=b.to(DEV), **kw)
         torch.cuda.synchronize()
         assert rms_rel_err(Yb, ref) <= BF16_RMS_REL and bf16_ulp_distance(Yb, ref) <= 1
+    if name.startswith("mfma") and dtype == "bf16":
+        assert cf.dense_variant_for(X.to(DEV), F.to(DEV), **kw) == cf.VARIANT_TILED
     # every variant that accepts the window gives the same contract
     for v in (cf.VARIANT_DIRECT, cf.VARIANT_TILED):
         try:
