@@ -176,6 +176,37 @@ def dw_runner(work, mode, exact):
     return Runner(work.name, make_set, launch, set_bytes, mode), flops, set_bytes
 
 
+def im2col_route_runner(work, mode, pack_only=False):
+    """The comparison route of the lecture's sections 5-7 on the same layer:
+    the explicit patch matrix (library kernel), then a library GEMM
+    (torch.matmul, i.e. hipBLASLt) of it with the reshaped filter. Timed with
+    the packing included; pack_only times the packing alone."""
+    import torch
+    import convolution_forward_amd as cf
+    import workloads as wl
+
+    X0, F0 = wl.dense_inputs(work)
+    Ho, Wo = work.H - work.KH + 1, work.W - work.KW + 1
+    M, K = work.N * Ho * Wo, work.KH * work.KW * work.Cin
+    set_bytes = (X0.numel() + F0.numel() + M * K + M * work.Cout) * 2
+
+    def make_set(i):
+        X = X0.to("cuda") if i == 0 else X0.to("cuda").clone()
+        F2 = F0.to("cuda").reshape(K, work.Cout).contiguous()
+        cols = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+        Y = torch.empty((M, work.Cout), dtype=torch.bfloat16, device="cuda")
+        return (X, F2, cols, Y)
+
+    def launch(st):
+        X, F2, cols, Y = st
+        cf.im2col_nhwc(X, work.KH, work.KW, out=cols)
+        if not pack_only:
+            torch.matmul(cols, F2, out=Y)
+
+    flops = 2.0 * M * work.Cout * K
+    return Runner(work.name + " im2col route", make_set, launch, set_bytes, mode), flops, set_bytes, M * K * 2
+
+
 def measure(runner, steps, warmup, trials, reps_cap=None):
     per_replay_target = 256
     reps = max(1, per_replay_target // len(runner.sets))
@@ -298,6 +329,20 @@ def main():
                               "frac_mfma_peak": round(tf / peak, 4), "mfma_peak": peak})
             del r
             torch.cuda.empty_cache()
+        # The explicit im2col route on the headline layer (packing included).
+        r, fl, by, cols_bytes = im2col_route_runner(wl.DENSE_3X3_BF16, args.mode)
+        m_route, n = measure(r, steps2, args.warmup, args.trials)
+        del r
+        torch.cuda.empty_cache()
+        r, _, _, _ = im2col_route_runner(wl.DENSE_3X3_BF16, args.mode, pack_only=True)
+        m_pack, _ = measure(r, steps2, args.warmup, args.trials)
+        del r
+        torch.cuda.empty_cache()
+        secondary.append({"workload": "dense3x3_bf16 via explicit im2col + library GEMM (comparison route)",
+                          "ms": m_route, "ms_packing": m_pack, "launches": n,
+                          "TFLOP/s": round(fl / (m_route * 1e-3) / 1e12, 2),
+                          "patch_matrix_bytes": cols_bytes,
+                          "implicit_gemm_ms": ms, "route_over_implicit": round(m_route / ms, 2)})
         for work_dw, exact in [(wl.DW_5X5S2_EXACT, True)] + [(l, False) for l in wl.DW_SWEEP]:
             r, fl, by = dw_runner(work_dw, args.mode, exact)
             m, n = measure(r, steps2, args.warmup, args.trials)

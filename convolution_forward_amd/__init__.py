@@ -45,7 +45,7 @@ VARIANT_TILED = 2
 EXPORTED = ("conv2d_nhwc_fwd", "conv2d_nhwc_fwd_variant", "conv2d_nhwc_fwd_window", "conv_depthwise_fwd",
             "conv_depthwise_fwd_variant", "conv_depthwise_fwd_window", "conv2d_nhwc_auto_variant",
             "conv2d_nhwc_window_auto_variant", "conv_depthwise_auto_variant", "conv_depthwise_window_auto_variant",
-            "conv_out_size", "conv_out_size_window", "conv_status_str", "conv_copy_bytes")
+            "conv_out_size", "conv_out_size_window", "conv_status_str", "conv_copy_bytes", "conv_im2col_nhwc")
 
 
 class ConvWindow(ctypes.Structure):
@@ -103,6 +103,8 @@ def load_library():
     lib.conv2d_nhwc_window_auto_variant.argtypes = [p, p] + [i] * 7 + [wp, i, i]
     lib.conv_depthwise_window_auto_variant.restype = i
     lib.conv_depthwise_window_auto_variant.argtypes = [i] * 7 + [wp]
+    lib.conv_im2col_nhwc.restype = i
+    lib.conv_im2col_nhwc.argtypes = [p, p, p] + [i] * 6 + [wp, i, p]
     lib.conv_out_size_window.restype = i64
     lib.conv_out_size_window.argtypes = [i64, i, i, i, i, i]
     lib.conv_status_str.restype = ctypes.c_char_p
@@ -261,6 +263,32 @@ def conv_depthwise(x, w, bias=None, stride=1, padding=0, dilation=1, exact: bool
                                        out.data_ptr(), N, C, H, W, mult, KH, KW, ctypes.byref(win), mode, variant,
                                        _stream_ptr(x.device))
     _check(st, "conv_depthwise_fwd_window")
+    return out
+
+
+def im2col_nhwc(x, KH: int, KW: int, stride=1, padding=0, dilation=1, out=None):
+    """Explicit patch matrix [N*Ho*Wo, KH*KW*Cin] of X on the GPU (see
+    include/convfwd.h): the packing step of the im2col route, for comparison
+    with the implicit-GEMM kernels, which never build it."""
+    torch = _torch()
+    lib = load_library()
+    _require_gpu(x, out)
+    if x.dim() != 4:
+        raise ValueError("expected X as [N,H,W,Cin]")
+    N, H, W, Cin = x.shape
+    win = window(stride, padding, dilation)
+    Ho = out_size_window(H, KH, win.stride_h, win.pad_top, win.pad_bottom, win.dil_h)
+    Wo = out_size_window(W, KW, win.stride_w, win.pad_left, win.pad_right, win.dil_w)
+    shape = (N * max(Ho, 0) * max(Wo, 0), KH * KW * Cin)
+    if out is None:
+        if Ho <= 0 or Wo <= 0:
+            _check(CONV_ERR_SHAPE, "conv_im2col_nhwc")
+        out = torch.empty(shape, dtype=x.dtype, device=x.device)
+    elif tuple(out.shape) != shape or not out.is_contiguous() or out.dtype != x.dtype:
+        raise ValueError(f"out must be a contiguous {x.dtype} tensor of shape {shape}")
+    st = lib.conv_im2col_nhwc(x.data_ptr(), _strides_arr(x), out.data_ptr(), N, H, W, Cin, KH, KW,
+                              ctypes.byref(win), _dtype_code(x.dtype), _stream_ptr(x.device))
+    _check(st, "conv_im2col_nhwc")
     return out
 
 

@@ -413,6 +413,45 @@ int conv_depthwise_auto_variant(int N, int C, int H, int W, int multiplier, int 
     return conv_depthwise_window_auto_variant(N, C, H, W, multiplier, KH, KW, &win);
 }
 
+conv_status conv_im2col_nhwc(const void *X, const int64_t *x_strides, void *cols, int N, int H, int W, int Cin,
+                             int KH, int KW, const conv_window *win, conv_dtype dtype, void *stream)
+{
+    if (!X || !cols || !win)
+        return CONV_ERR_NULL;
+    if (win->groups != 1)
+        return CONV_ERR_UNSUPPORTED;
+    // The dense checks with Cout = 1 give the output shape and X's layout.
+    DenseProblem d;
+    const conv_status st = check_dense_shape(x_strides, nullptr, N, H, W, Cin, KH, KW, 1, *win, dtype, dtype, &d);
+    if (st != CONV_OK)
+        return st;
+    const int64_t xdims[4] = {N, H, W, Cin};
+    const int64_t cols_bytes = (int64_t)N * d.Ho * d.Wo * KH * KW * Cin * dtype_size(dtype);
+    if (overlaps(flat_range(cols, cols_bytes), strided_range(X, xdims, d.xs, dtype_size(dtype))))
+        return CONV_ERR_ALIAS;
+    Im2colProblem p;
+    p.X = X;
+    for (int k = 0; k < 4; ++k)
+        p.xs[k] = d.xs[k];
+    p.cols = cols;
+    p.N = N;
+    p.H = H;
+    p.W = W;
+    p.Cin = Cin;
+    p.KH = KH;
+    p.KW = KW;
+    p.Ho = d.Ho;
+    p.Wo = d.Wo;
+    p.sh = d.sh;
+    p.sw = d.sw;
+    p.pt = d.pt;
+    p.pl = d.pl;
+    p.dh = d.dh;
+    p.dw = d.dw;
+    p.dtype = dtype;
+    return launched(launch_im2col(p, (hipStream_t)stream));
+}
+
 conv_status conv_copy_bytes(const void *src, void *dst, int64_t bytes, void *stream)
 {
     if (!src || !dst)

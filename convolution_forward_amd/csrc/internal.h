@@ -56,6 +56,19 @@ hipError_t launch_dw_direct(const DwProblem &p, hipStream_t s);
 bool dw_tiled_supports(const DwProblem &p);
 hipError_t launch_dw_tiled(const DwProblem &p, hipStream_t s);
 
+// A validated explicit patch-matrix problem: NHWC X with element strides,
+// cols contiguous [N*Ho*Wo, KH*KW*Cin] of the same dtype.
+struct Im2colProblem {
+    const void *X;
+    int64_t xs[4];
+    void *cols;
+    int N, H, W, Cin, KH, KW, Ho, Wo;
+    int sh, sw, pt, pl, dh, dw;
+    conv_dtype dtype;
+};
+
+hipError_t launch_im2col(const Im2colProblem &p, hipStream_t s);
+
 // Streaming copy used for bandwidth / counter calibration.
 hipError_t launch_copy_bytes(const void *src, void *dst, int64_t bytes, hipStream_t s);
 

@@ -210,6 +210,34 @@ CONVFWD_API conv_status conv_depthwise_fwd_window(const float *X, const float *w
                                       int C, int H, int W, int multiplier, int KH, int KW,
                                       const conv_window *win, conv_dw_mode mode, int variant, void *stream);
 
+/*
+ * conv_im2col_nhwc -- the explicit patch matrix of the dense operator.
+ *
+ * "CMU DLSys Lecture 14", section 5: row m = (n*Ho + y)*Wo + x holds the
+ * KH*KW*Cin input values output (n, y, x) reads, in (i, j, c) order, so that
+ * cols @ F.reshape(KH*KW*Cin, Cout) is the convolution. Section 6 prices
+ * this copy; section 7 asks that a timing of the matrix route include it.
+ * The convolution entry points never build it; this call exists for that
+ * comparison. With a window, tap (i, j) of output (y, x) reads input row
+ * y*stride_h + i*dil_h - pad_top and column x*stride_w + j*dil_w - pad_left,
+ * and taps in the padding are zeros.
+ *
+ *   X         device, logical NHWC [N,H,W,Cin], channel stride 1 (x_strides
+ *             as for conv2d_nhwc_fwd, NULL = contiguous), dtype `dtype`.
+ *   cols      device, contiguous [N*Ho*Wo, KH*KW*Cin], dtype `dtype`, caller
+ *             owned (this is the storage the explicit route costs), fully
+ *             overwritten.
+ *   win       host pointer, not NULL; win->groups must be 1.
+ *   dtype     CONV_F32 or CONV_BF16; values are copied bit for bit.
+ *
+ * Errors: CONV_ERR_NULL, CONV_ERR_NONPOSITIVE, CONV_ERR_SHAPE (Ho or Wo
+ * <= 0), CONV_ERR_DTYPE, CONV_ERR_LAYOUT (channel stride != 1),
+ * CONV_ERR_UNSUPPORTED (groups != 1), CONV_ERR_ALIAS (cols overlaps X),
+ * CONV_ERR_HIP.
+ */
+CONVFWD_API conv_status conv_im2col_nhwc(const void *X, const int64_t *x_strides, void *cols, int N, int H, int W,
+                             int Cin, int KH, int KW, const conv_window *win, conv_dtype dtype, void *stream);
+
 /* Which variant CONV_VARIANT_AUTO would launch for these dense / depthwise
  * arguments (a CONV_VARIANT_* value), or -1 if the arguments are invalid.
  * Host-only; makes no HIP call. */

@@ -226,3 +226,19 @@ def test_window_auto_variants(lib):
     dq = lambda win: lib.conv_depthwise_window_auto_variant(8, 72, 56, 56, 1, 5, 5, ctypes.byref(win))
     assert dq(W(stride=2, padding=2)) == lib.conv_depthwise_auto_variant(8, 72, 56, 56, 1, 5, 5, 2, 2, 2, 2, 1, 1)
     assert dq(W(groups=2)) == -1
+
+
+def test_im2col_errors(lib):
+    XA, CA = 0x10000000, 0x50000000
+    W = cf.window
+    call = lambda X, cols, win, **k: lib.conv_im2col_nhwc(
+        X, None, cols, k.get("N", 1), k.get("H", 6), k.get("Wd", 6), k.get("Cin", 4), k.get("KH", 3), k.get("KW", 3),
+        ctypes.byref(win) if win is not None else None, k.get("dt", cf.CONV_F32), None)
+    assert call(0, CA, W()) == cf.CONV_ERR_NULL
+    assert call(XA, 0, W()) == cf.CONV_ERR_NULL
+    assert call(XA, CA, None) == cf.CONV_ERR_NULL
+    assert call(XA, CA, W(groups=2)) == cf.CONV_ERR_UNSUPPORTED
+    assert call(XA, CA, W(), H=2) == cf.CONV_ERR_SHAPE
+    assert call(XA, CA, W(), Cin=0) == cf.CONV_ERR_NONPOSITIVE
+    assert call(XA, CA, W(), dt=7) == cf.CONV_ERR_DTYPE
+    assert call(XA, XA + 64, W()) == cf.CONV_ERR_ALIAS
