@@ -207,6 +207,73 @@ def im2col_route_runner(work, mode, pack_only=False):
     return Runner(work.name + " im2col route", make_set, launch, set_bytes, mode), flops, set_bytes, M * K * 2
 
 
+# Windowed layers (stride, padding, groups, 1D) measured beside the headline:
+# name, X [N,H,W,Cin], (KH, KW, Cout), stride, padding, groups, dtype.
+WINDOW_LAYERS = [
+    ("dense3x3_bf16 same (pad 1)", (32, 56, 56, 64), (3, 3, 64), 1, 1, 1, "bf16"),
+    ("dense3x3_bf16 stride 2 pad 1 -> 128 ch", (32, 56, 56, 64), (3, 3, 128), 2, 1, 1, "bf16"),
+    ("grouped3x3_bf16 8 groups (pad 1)", (32, 56, 56, 128), (3, 3, 128), 1, 1, 8, "bf16"),
+    ("conv1d_bf16 K3 stride 2 pad 1 (Conv1D stem, 384 ch, 3000 frames)", (8, 1, 3000, 384), (1, 3, 384), (1, 2),
+     (0, 1), 1, "bf16"),
+]
+# Causal depthwise Conv1D: N, C, L, K (all padding before the signal), fast mode.
+CAUSAL_DW = ("dw_causal_conv1d K4 (512 ch, 4096 steps)", 16, 512, 4096, 4)
+
+
+def window_runner(layer, mode):
+    import torch
+    import convolution_forward_amd as cf
+    import workloads as wl
+
+    name, (N, H, W, C), (KH, KW, O), stride, padding, groups, dt = layer
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    X0 = wl.random_tensor((N, H, W, C), 500).to(tdt)
+    F0 = (wl.random_tensor((KH, KW, C // groups, O), 501) * (1.0 / (KH * KW * C / groups) ** 0.5)).to(tdt)
+    win = cf.window(stride, padding, 1, groups)
+    Ho = cf.out_size_window(H, KH, win.stride_h, win.pad_top, win.pad_bottom, 1)
+    Wo = cf.out_size_window(W, KW, win.stride_w, win.pad_left, win.pad_right, 1)
+    esz = X0.element_size()
+    set_bytes = (X0.numel() + F0.numel() + N * Ho * Wo * O) * esz
+
+    def make_set(i):
+        X = X0.to("cuda") if i == 0 else X0.to("cuda").clone()
+        F = F0.to("cuda")
+        Y = torch.empty((N, Ho, Wo, O), dtype=tdt, device="cuda")
+        return (X, F, Y)
+
+    def launch(st):
+        X, F, Y = st
+        cf.conv2d_nhwc(X, F, out=Y, stride=stride, padding=padding, groups=groups)
+
+    flops = 2.0 * N * Ho * Wo * O * KH * KW * C / groups
+    r = Runner(name, make_set, launch, set_bytes, mode)
+    variant = cf.dense_variant_for(X0[:1].to("cuda"), F0.to("cuda"), stride=stride, padding=padding, groups=groups)
+    return r, flops, set_bytes, {1: "direct", 2: "mfma_implicit_gemm"}.get(variant)
+
+
+def causal_dw_runner(mode):
+    import torch
+    import convolution_forward_amd as cf
+    import workloads as wl
+
+    name, N, C, L, K = CAUSAL_DW
+    X0 = wl.random_tensor((N, C, 1, L), 510)
+    w0 = wl.random_tensor((C, 1, K), 511)
+    set_bytes = (2 * X0.numel() + w0.numel()) * 4
+
+    def make_set(i):
+        X = X0.to("cuda") if i == 0 else X0.to("cuda").clone()
+        return (X, w0.to("cuda"), torch.empty_like(X, device="cuda"))
+
+    def launch(st):
+        X, w, Y = st
+        cf.conv_depthwise(X, w, padding=(0, 0, K - 1, 0), exact=False, out=Y)
+
+    variant = cf.depthwise_variant_for((N, C, 1, L), (C, 1, K), 1, (0, 0, K - 1, 0))
+    return Runner(name, make_set, launch, set_bytes, mode), 2.0 * N * C * L * K, set_bytes, \
+        {1: "direct", 2: "lds_tiled"}.get(variant)
+
+
 def measure(runner, steps, warmup, trials, reps_cap=None):
     per_replay_target = 256
     reps = max(1, per_replay_target // len(runner.sets))
@@ -343,6 +410,23 @@ def main():
                           "TFLOP/s": round(fl / (m_route * 1e-3) / 1e12, 2),
                           "patch_matrix_bytes": cols_bytes,
                           "implicit_gemm_ms": ms, "route_over_implicit": round(m_route / ms, 2)})
+        for layer in WINDOW_LAYERS:
+            r, fl, by, kv = window_runner(layer, args.mode)
+            m, n = measure(r, max(100, steps2 // 2), args.warmup, args.trials)
+            tf = fl / (m * 1e-3) / 1e12
+            gb = by / (m * 1e-3) / 1e9
+            secondary.append({"workload": layer[0], "kernel": kv, "ms": m, "launches": n, "TFLOP/s": round(tf, 2),
+                              "GB/s": round(gb, 1), "frac_hbm": round(gb / HBM_PEAK_GBS, 4),
+                              "frac_mfma_peak": round(tf / BF16_MFMA_PEAK_TFLOPS, 4)})
+            del r
+            torch.cuda.empty_cache()
+        r, fl, by, kv = causal_dw_runner(args.mode)
+        m, n = measure(r, steps2, args.warmup, args.trials)
+        gb = by / (m * 1e-3) / 1e9
+        secondary.append({"workload": CAUSAL_DW[0], "kernel": kv, "ms": m, "launches": n, "GB/s": round(gb, 1),
+                          "frac_hbm": round(gb / HBM_PEAK_GBS, 4), "GFLOP/s": round(fl / (m * 1e-3) / 1e9, 1)})
+        del r
+        torch.cuda.empty_cache()
         for work_dw, exact in [(wl.DW_5X5S2_EXACT, True)] + [(l, False) for l in wl.DW_SWEEP]:
             r, fl, by = dw_runner(work_dw, args.mode, exact)
             m, n = measure(r, steps2, args.warmup, args.trials)
