@@ -82,6 +82,8 @@ struct RowArgs {
     int row_elems;      // LDS elements per staged input row (row_slots * pitch)
     int chunks_per_row; // 16-byte chunks of real input per row (W * Cin_padded / 8)
     int otile_off;      // LDS byte offset of the output tiles
+    int rows_off;       // LDS element offset of the row buffers: 0 (they reuse the
+                        // filter staging area) or past the staging area
     uint32_t x_records; // bytes addressable from one image's base in X
     uint32_t y_records; // bytes addressable from one image's base in Y
 };
@@ -258,13 +260,14 @@ void dense_rows_mfma(RowArgs a)
     constexpr int OCH = COUT_TILE * ESZ / 16;                        // 16-byte chunks per pixel
     constexpr int OSTORE = (64 * BPW * OCH + THREADS - 1) / THREADS;  // store instructions per row
 
-    // LDS: [filter staging, later two input-row buffers] [output tiles]. The
-    // filter staging area is dead once the fragments are in registers; input
-    // row r is then committed into buffer r & 1 (the host sizes the area for
-    // both uses).
+    // LDS: [filter staging] [two input-row buffers] [output tiles], or, when
+    // that does not fit, [filter staging, later the row buffers] [output
+    // tiles]: the staging area is dead once the fragments are in registers.
+    // Input row r lives in buffer r & 1.
     extern __shared__ __align__(16) uint16_t smem[];
     uint16_t *ft = smem;
-    uint16_t *rows = smem;
+    uint16_t *rows = smem + a.rows_off;
+    const bool rows_apart = a.rows_off != 0;
     uint8_t *otile = reinterpret_cast<uint8_t *>(smem) + a.otile_off;
 
     const int tid = threadIdx.x;
@@ -322,16 +325,13 @@ void dense_rows_mfma(RowArgs a)
             xin[i][k] = __builtin_amdgcn_raw_buffer_load_b128(
                 xr, chunk_off<CINP>(a, iy0 + i, tid + k * THREADS, iy_end), 0, 0);
 
-    // 3. Filter slice into LDS, then 4. its A fragments into registers.
-    filt.commit(ft, tid);
-    __syncthreads();
-    bf16x8 wf[KSTEPS][NBW];
-    FilterSlice<KH, KW, CS>::fragments(ft, lane, half, wf);
-    __syncthreads();      // the staging area becomes the input-row area
-
-    // 5. Zero the padding slots of both row buffers (never overwritten
-    //    afterwards), and input row 0 into buffer 0.
-    {
+    // 3. Filter slice into LDS; 4. zero the padding slots of both row
+    //    buffers (never overwritten afterwards) and commit input row 0 into
+    //    buffer 0; 5. the A fragments into registers. With the rows apart
+    //    from the staging area, 3 and 4 share one barrier and the loop can
+    //    start right after 5; otherwise 4 waits until every wave has read its
+    //    fragments.
+    auto commit_first_row = [&]() __attribute__((always_inline)) {
         const int zslots = a.row_slots - a.W;
         for (int q = tid; q < 2 * zslots * CG; q += THREADS) {
             const int b = q / (zslots * CG);
@@ -340,14 +340,24 @@ void dense_rows_mfma(RowArgs a)
             const int slot = zi < a.pl ? zi : zi + a.W;
             *reinterpret_cast<u32x4 *>(rows + b * a.row_elems + slot * PITCH + (zq - zi * CG) * 8) = u32x4{0, 0, 0, 0};
         }
-    }
 #pragma unroll
-    for (int k = 0; k < MAXC; ++k) {
-        const int q = tid + k * THREADS;
-        if (q < a.chunks_per_row)
-            put_chunk<CINP, S>(rows, a.pl, q, xin[0][k]);
-    }
+        for (int k = 0; k < MAXC; ++k) {
+            const int q = tid + k * THREADS;
+            if (q < a.chunks_per_row)
+                put_chunk<CINP, S>(rows, a.pl, q, xin[0][k]);
+        }
+    };
+    filt.commit(ft, tid);
+    if (rows_apart)
+        commit_first_row();
     __syncthreads();
+    bf16x8 wf[KSTEPS][NBW];
+    FilterSlice<KH, KW, CS>::fragments(ft, lane, half, wf);
+    if (!rows_apart) {
+        __syncthreads();      // the staging area becomes the input-row area
+        commit_first_row();
+        __syncthreads();
+    }
 
     // A finished output row leaves as 16-byte chunks from its LDS tile:
     // consecutive lanes write consecutive bytes of consecutive pixels, so
@@ -504,7 +514,7 @@ constexpr bool wide_rows_ok(int KH) { return KH == 1; }
 
 struct Plan {
     int S, CS, BPW, MAXC, NR, R, slots;
-    size_t otile_off, lds;
+    size_t rows_off, otile_off, lds;
 };
 
 // Bytes addressable from one image's base: the extent of the last element.
@@ -568,12 +578,20 @@ bool plan_rows(const DenseProblem &p, Plan *plan)
     // A staged row holds the pixels the outputs read and every real pixel.
     const int need = (p.Wo - 1) * pl.S + p.KW;
     pl.slots = need > p.pl + p.W ? need : p.pl + p.W;
-    // LDS: [max(filter staging, two input rows)] [two output tiles].
+    // LDS: [filter staging] [two input rows] [two output tiles] when it
+    // fits, else [max(filter staging, two input rows)] [two output tiles].
     const size_t pitch = pl.S == 1 ? (size_t)32 * pl.CS + 16 : (size_t)32 * pl.CS + 8;
     const size_t filt = (size_t)p.KH * p.KW * 32 * pl.CS * (COUT_TILE + 8) * 2;
     const size_t rows = (size_t)2 * pl.slots * pitch * 2;
-    pl.otile_off = filt > rows ? filt : rows;
-    pl.lds = pl.otile_off + 2 * (size_t)64 * pl.BPW * (COUT_TILE * yesz + 32);
+    const size_t otiles = 2 * (size_t)64 * pl.BPW * (COUT_TILE * yesz + 32);
+    if (filt + rows + otiles <= (size_t)LDS_BYTES_MAX) {
+        pl.rows_off = filt;
+        pl.otile_off = filt + rows;
+    } else {
+        pl.rows_off = 0;
+        pl.otile_off = filt > rows ? filt : rows;
+    }
+    pl.lds = pl.otile_off + otiles;
     if (pl.lds > (size_t)LDS_BYTES_MAX)
         return false;
     *plan = pl;
@@ -716,6 +734,7 @@ hipError_t launch_dense_mfma_bf16(const DenseProblem &p0, hipStream_t s)
     a.row_elems = plan.slots * (plan.S == 1 ? 32 * plan.CS + 16 : 32 * plan.CS + 8);
     a.chunks_per_row = p.W * 32 * plan.CS / 8;
     a.otile_off = (int)plan.otile_off;
+    a.rows_off = (int)(plan.rows_off / 2);
     a.x_records = (uint32_t)image_extent(p.xs, p.H, p.W, p.Cin, 2);
     a.y_records = (uint32_t)image_extent(p.ys, p.Ho, p.Wo, p.Cout, p.ydt == CONV_BF16 ? 2 : 4);
     a.R = plan.R;
