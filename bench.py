@@ -274,6 +274,25 @@ def causal_dw_runner(mode):
         {1: "direct", 2: "lds_tiled"}.get(variant)
 
 
+def copy_runner(nbytes, mode):
+    """The plain copy kernel moving nbytes/2 in and nbytes/2 out per launch:
+    what the memory system delivers at this size and cache state."""
+    import torch
+    import convolution_forward_amd as cf
+
+    half = (int(nbytes) // 2 + 15) // 16 * 16
+
+    def make_set(i):
+        src = torch.empty(half, dtype=torch.uint8, device="cuda")
+        src.fill_(1)
+        return (src, torch.empty(half, dtype=torch.uint8, device="cuda"))
+
+    def launch(st):
+        cf.copy_bytes(st[0], st[1])
+
+    return Runner("copy", make_set, launch, 2 * half, mode), 2 * half
+
+
 def measure(runner, steps, warmup, trials, reps_cap=None):
     per_replay_target = 256
     reps = max(1, per_replay_target // len(runner.sets))
@@ -377,6 +396,15 @@ def main():
                      "mfma_frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4)},
     }
     line["config"]["buffer_sets"] = max(1, math.ceil(COLD_BYTES / set_bytes)) if args.mode == "cold" else 1
+    # Context for the HBM fraction: a plain copy of the same number of bytes,
+    # in the same cache state, is what the memory system delivers at this size.
+    r, cb = copy_runner(set_bytes, args.mode)
+    m_copy, _ = measure(r, args.steps, args.warmup, args.trials)
+    del r
+    torch.cuda.empty_cache()
+    line["roofline"]["copy_same_bytes_ms"] = m_copy
+    line["roofline"]["copy_same_bytes_GBps"] = round(cb / (m_copy * 1e-3) / 1e9, 1)
+    line["roofline"]["frac_of_copy"] = round(m_copy / ms, 4)
 
     secondary = []
     if not args.no_secondary:

@@ -233,8 +233,13 @@ __global__ __launch_bounds__(THREADS) void dw_tiled_kernel(TileArgs a)
 struct TilePlan {
     int RT, PPW, bands, RB, TPP;
     int64_t lds_elems;
-    double util;
+    double util;        // fraction of thread-row slots that hold an output
+    double score;       // util, discounted when the grid is too small to hide latency
 };
+
+// Waves (three per SIMD of the 1024) below which a launch cannot keep enough
+// loads in flight or overlap one wave's arithmetic with another's waiting.
+constexpr double WAVES_WANTED = 3.0 * 1024;
 
 // Tile shape for rows-per-thread RT: whole planes when a plane's outputs fit
 // one workgroup, else bands of rows of one plane. A constant of the shape.
@@ -271,6 +276,8 @@ TilePlan plan_for(const DwProblem &p, int RT)
     const int64_t tiles = (planes + t.PPW - 1) / t.PPW * t.bands;
     const double slots = (double)tiles * THREADS * RT;
     t.util = (double)planes * p.Ho * p.Wo / slots;
+    const double waves = (double)tiles * THREADS / 64;
+    t.score = t.util * (waves < WAVES_WANTED ? waves / WAVES_WANTED : 1.0);
     return t;
 }
 
@@ -292,11 +299,13 @@ bool plan(const DwProblem &p, TilePlan &out)
     if (planes >= (1ll << 31) - THREADS || planes * p.Ho * p.Wo >= (1ll << 40))
         return false;
     bool have = false;
-    for (int RT : {4, 7}) {
+    // Rows per thread: more rows reuse each LDS value for more outputs,
+    // fewer rows give more waves. Take the best score; on a tie, more rows.
+    for (int RT : {2, 4, 7}) {
         TilePlan t = plan_for(p, RT);
         if (t.lds_elems * 4 > LDS_LIMIT)
             continue;
-        if (!have || t.util > out.util + 1e-9 || (t.util > out.util - 1e-9 && RT > out.RT)) {
+        if (!have || t.score > out.score + 1e-9 || (t.score > out.score - 1e-9 && RT > out.RT)) {
             out = t;
             have = true;
         }
@@ -322,7 +331,11 @@ hipError_t launch_rt(const TileArgs &a, unsigned grid, size_t lds, bool exact, h
 template <int KH, int KW, int S>
 hipError_t launch_s(const TileArgs &a, int RT, unsigned grid, size_t lds, bool exact, hipStream_t s)
 {
-    return RT == 4 ? launch_rt<KH, KW, S, 4>(a, grid, lds, exact, s) : launch_rt<KH, KW, S, 7>(a, grid, lds, exact, s);
+    switch (RT) {
+    case 2: return launch_rt<KH, KW, S, 2>(a, grid, lds, exact, s);
+    case 4: return launch_rt<KH, KW, S, 4>(a, grid, lds, exact, s);
+    default: return launch_rt<KH, KW, S, 7>(a, grid, lds, exact, s);
+    }
 }
 
 template <int KH, int KW>
