@@ -228,6 +228,102 @@ __global__ __launch_bounds__(THREADS) void dw_tiled_kernel(TileArgs a)
     }
 }
 
+// Filters one row tall (1D along the width: causal and strided Conv1D over
+// a sequence, "Convolution Is Wx+b Moving Across a Signal", section "Where
+// this shows up in models I work with"). Planes are single rows here, so a
+// workgroup takes a segment of SEG outputs of one output row instead of
+// whole planes: it copies the input span the segment reads (zeros outside
+// the row) into LDS with one 4-byte load per element, then each thread
+// computes V consecutive outputs with the same arithmetic, in the same
+// order, as the kernels above.
+constexpr int ROW_V = 4;                          // outputs per thread
+constexpr int ROW_SEG = THREADS * ROW_V;          // outputs per workgroup
+
+struct RowArgs1d {
+    const float *X;
+    const float *w;
+    const float *bias;
+    float *Y;
+    int64_t XE;              // elements of X
+    int C, H, W, mult, Cout, Ho, Wo, sh, pt, pl;
+    int segs;                // segments per output row
+    int span;                // input elements a full segment reads
+    FastDiv div_segs, div_ho, div_cout, div_mult;
+};
+
+template <int KW, int S, int EXACT>
+__global__ __launch_bounds__(THREADS) void dw_row1d_kernel(RowArgs1d a)
+{
+#pragma clang fp contract(off)
+    extern __shared__ __align__(16) float lds[];
+    const int tid = threadIdx.x;
+    // Output row (n, oc, oy) and segment.
+    const uint32_t row = fdiv(blockIdx.x, a.div_segs);
+    const int seg = (int)(blockIdx.x - row * (uint32_t)a.segs);
+    const uint32_t plane = fdiv(row, a.div_ho);            // n * Cout + oc
+    const int oy = (int)(row - plane * (uint32_t)a.Ho);
+    const uint32_t n = fdiv(plane, a.div_cout);
+    const int oc = (int)(plane - n * (uint32_t)a.Cout);
+    const int ic = (int)fdiv((uint32_t)oc, a.div_mult);
+    const int iy = oy * a.sh - a.pt;                         // the input row (KH = 1)
+    const bool row_in = iy >= 0 && iy < a.H;
+    const int ox0 = seg * ROW_SEG;
+    const int c0 = ox0 * S - a.pl;                           // input column of LDS element 0
+
+    float wv[KW];
+#pragma unroll
+    for (int k = 0; k < KW; ++k)
+        wv[k] = a.w[(int64_t)oc * KW + k];
+
+    // Input span into LDS: element e is column c0 + e of input row iy, or
+    // +0 outside the row (the padding the definition multiplies).
+    const int64_t rbase = (((int64_t)n * a.C + ic) * a.H + (row_in ? iy : 0)) * a.W;
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float *>(a.X + rbase), 0, a.W * 4, BUF_WORD3);
+    constexpr int LOADS = (ROW_SEG * S + KW + THREADS - 1) / THREADS;
+    float v[LOADS];
+#pragma unroll
+    for (int u = 0; u < LOADS; ++u) {
+        const int e = tid + u * THREADS;
+        const int col = c0 + e;
+        const bool ok = row_in && e < a.span && col >= 0 && col < a.W;
+        v[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(xr, ok ? (uint32_t)col * 4 : OOB, 0, 0));
+    }
+#pragma unroll
+    for (int u = 0; u < LOADS; ++u) {
+        const int e = tid + u * THREADS;
+        if (e < a.span)
+            lds[e] = v[u];
+    }
+    __syncthreads();
+
+    const float bv = a.bias ? a.bias[oc] : 0.0f;
+    float *yrow = a.Y + (int64_t)row * a.Wo;
+#pragma unroll
+    for (int q = 0; q < ROW_V; ++q) {
+        const int j = tid * ROW_V + q;                       // output within the segment
+        const int ox = ox0 + j;
+        if (ox < a.Wo) {
+            float acc = +0.0f;
+#pragma unroll
+            for (int kx = 0; kx < KW; ++kx) {
+                const float xv = lds[j * S + kx];
+                if constexpr (EXACT) {
+                    const float prod = wv[kx] * xv;
+                    acc = acc + prod;
+                } else {
+                    acc = __builtin_fmaf(wv[kx], xv, acc);
+                }
+            }
+            if (a.bias)
+                acc = acc + bv;
+            if (EXACT && __builtin_isnan(acc))
+                acc = __uint_as_float(0x7FC00000u);
+            yrow[ox] = acc;
+        }
+    }
+}
+
 // --- host side -------------------------------------------------------------
 
 struct TilePlan {
@@ -279,6 +375,63 @@ TilePlan plan_for(const DwProblem &p, int RT)
     const double waves = (double)tiles * THREADS / 64;
     t.score = t.util * (waves < WAVES_WANTED ? waves / WAVES_WANTED : 1.0);
     return t;
+}
+
+// The row kernel takes filters one row tall with 3, 4 or 5 taps, unit
+// dilation and a stride of 1 or 2 along the width.
+bool row1d_takes(const DwProblem &p)
+{
+    if (p.KH != 1 || (p.KW != 3 && p.KW != 4 && p.KW != 5) || p.dw != 1 || (p.sw != 1 && p.sw != 2))
+        return false;
+    const int64_t rows = (int64_t)p.N * p.C * p.mult * p.Ho;
+    const int64_t segs = (p.Wo + ROW_SEG - 1) / ROW_SEG;
+    return rows * segs < (int64_t(1) << 31) && (int64_t)p.N * p.C * p.H * p.W < (int64_t(1) << 40) &&
+           p.W < (1 << 29);
+}
+
+template <int KW, int S>
+hipError_t launch_row1d_k(const RowArgs1d &a, unsigned grid, size_t lds, bool exact, hipStream_t s)
+{
+    if (exact)
+        hipLaunchKernelGGL((dw_row1d_kernel<KW, S, 1>), dim3(grid), dim3(THREADS), lds, s, a);
+    else
+        hipLaunchKernelGGL((dw_row1d_kernel<KW, S, 0>), dim3(grid), dim3(THREADS), lds, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_row1d(const DwProblem &p, hipStream_t s)
+{
+    RowArgs1d a;
+    a.X = p.X;
+    a.w = p.w;
+    a.bias = p.bias;
+    a.Y = p.Y;
+    a.XE = (int64_t)p.N * p.C * p.H * p.W;
+    a.C = p.C;
+    a.H = p.H;
+    a.W = p.W;
+    a.mult = p.mult;
+    a.Cout = p.C * p.mult;
+    a.Ho = p.Ho;
+    a.Wo = p.Wo;
+    a.sh = p.sh;
+    a.pt = p.ph;
+    a.pl = p.pw;
+    a.segs = (p.Wo + ROW_SEG - 1) / ROW_SEG;
+    a.span = (ROW_SEG - 1) * p.sw + p.KW;
+    a.div_segs = make_fastdiv((uint32_t)a.segs);
+    a.div_ho = make_fastdiv((uint32_t)p.Ho);
+    a.div_cout = make_fastdiv((uint32_t)a.Cout);
+    a.div_mult = make_fastdiv((uint32_t)p.mult);
+    const int64_t grid = (int64_t)p.N * a.Cout * p.Ho * a.segs;
+    const size_t lds = (size_t)a.span * 4;
+    const bool exact = p.mode == CONV_DW_EXACT;
+    const bool s2 = p.sw == 2;
+    switch (p.KW) {
+    case 3: return s2 ? launch_row1d_k<3, 2>(a, (unsigned)grid, lds, exact, s) : launch_row1d_k<3, 1>(a, (unsigned)grid, lds, exact, s);
+    case 4: return s2 ? launch_row1d_k<4, 2>(a, (unsigned)grid, lds, exact, s) : launch_row1d_k<4, 1>(a, (unsigned)grid, lds, exact, s);
+    default: return s2 ? launch_row1d_k<5, 2>(a, (unsigned)grid, lds, exact, s) : launch_row1d_k<5, 1>(a, (unsigned)grid, lds, exact, s);
+    }
 }
 
 bool plan(const DwProblem &p, TilePlan &out)
@@ -349,11 +502,13 @@ hipError_t launch_k(const TileArgs &a, int S, int RT, unsigned grid, size_t lds,
 bool dw_tiled_supports(const DwProblem &p)
 {
     TilePlan t;
-    return plan(p, t);
+    return row1d_takes(p) || plan(p, t);
 }
 
 hipError_t launch_dw_tiled(const DwProblem &p, hipStream_t s)
 {
+    if (row1d_takes(p))
+        return launch_row1d(p, s);
     TilePlan t;
     if (!plan(p, t))
         return hipErrorNotSupported;

@@ -102,6 +102,11 @@ DW = [  # name, (N,C,H,W), mult, (KH,KW), stride, padding (t,b,l,r), dilation
     ("same_even_stride2", (2, 12, 28, 28), 1, (3, 3), 2, (0, 1, 0, 1), 1),
     ("asym_5x5", (1, 6, 19, 22), 1, (5, 5), 1, (2, 1, 0, 3), 1),
     ("asym_tiled_3x3", (2, 8, 30, 32), 1, (3, 3), 2, (1, 0, 1, 0), 1),
+    # one-row filters on the row kernel: several segments, ragged tails,
+    # stride 2, multiplier 2, rows of pure padding above the input
+    ("row_causal_long", (1, 3, 1, 5000), 1, (1, 4), 1, (0, 0, 3, 0), 1),
+    ("row_stride2_k5", (2, 6, 1, 333), 2, (1, 5), (1, 2), (0, 0, 2, 2), 1),
+    ("row_rows_k3", (1, 4, 5, 2100), 1, (1, 3), (2, 1), (1, 0, 1, 1), 1),
 ]
 
 
@@ -135,5 +140,5 @@ def test_gpu_depthwise_window_bitwise(case, mode):
             np.testing.assert_array_equal(gn, rn)
             np.testing.assert_array_equal(g[~gn], r[~rn])
         outs.append(Y)
-    if name == "asym_tiled_3x3":
+    if name == "asym_tiled_3x3" or name.startswith("row_") or name == "causal_dw_conv1d":
         assert cf.depthwise_variant_for((N, C, H, W), (C * m, KH, KW), stride, padding, dilation) == cf.VARIANT_TILED
