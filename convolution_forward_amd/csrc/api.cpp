@@ -160,13 +160,19 @@ conv_status validate_dense(const void *X, const int64_t *x_strides, const void *
 bool dense_tiled_supports(const DenseProblem &p)
 {
     if (p.xdt == CONV_BF16)
-        return dense_mfma_bf16_supports(p);
+        return dense_mfma_bf16_supports(p) || dense_gemm_bf16_supports(p);
     return plain_window(p) && dense_mfma_f32_supports(p);
 }
 
+// bf16: the row kernel where its plan fits (band rows in LDS, filter in
+// registers), else the streamed-filter GEMM kernel.
 hipError_t launch_dense_tiled(const DenseProblem &p, hipStream_t s)
 {
-    return p.xdt == CONV_BF16 ? launch_dense_mfma_bf16(p, s) : launch_dense_mfma_f32(p, s);
+    if (p.xdt != CONV_BF16)
+        return launch_dense_mfma_f32(p, s);
+    if (dense_mfma_bf16_supports(p))
+        return launch_dense_mfma_bf16(p, s);
+    return launch_dense_gemm_bf16(p, s);
 }
 
 int dense_auto(const DenseProblem &p) { return dense_tiled_supports(p) ? CONV_VARIANT_TILED : CONV_VARIANT_DIRECT; }

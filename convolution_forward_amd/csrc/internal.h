@@ -48,6 +48,8 @@ struct DwProblem {
 hipError_t launch_dense_direct(const DenseProblem &p, hipStream_t s);
 bool dense_mfma_bf16_supports(const DenseProblem &p);
 hipError_t launch_dense_mfma_bf16(const DenseProblem &p, hipStream_t s);
+bool dense_gemm_bf16_supports(const DenseProblem &p);
+hipError_t launch_dense_gemm_bf16(const DenseProblem &p, hipStream_t s);
 bool dense_mfma_f32_supports(const DenseProblem &p);
 hipError_t launch_dense_mfma_f32(const DenseProblem &p, hipStream_t s);
 

@@ -214,15 +214,17 @@ def test_out_size_window(lib):
 
 
 def test_window_auto_variants(lib):
-    """A window other than the lecture's goes to the direct kernel; the plain
-    window through the window entry point is routed like conv2d_nhwc_fwd."""
+    """bf16 windows of any shape go to a matrix-core kernel (a dilated window
+    to the streamed-filter GEMM); fp32 operands take the matrix cores only
+    for the lecture's plain window. The plain window through the window entry
+    point is routed like conv2d_nhwc_fwd."""
     W = cf.window
-    q = lambda win, **k: lib.conv2d_nhwc_window_auto_variant(
-        None, XA, k.get("N", 2), k.get("H", 12), k.get("Wd", 12), 64, 3, 3, 64, ctypes.byref(win),
-        cf.CONV_BF16, cf.CONV_BF16)
+    q = lambda win, dt=cf.CONV_BF16, **k: lib.conv2d_nhwc_window_auto_variant(
+        None, XA, k.get("N", 2), k.get("H", 12), k.get("Wd", 12), 64, 3, 3, 64, ctypes.byref(win), dt, dt)
     assert q(W()) == lib.conv2d_nhwc_auto_variant(None, XA, 2, 12, 12, 64, 3, 3, 64, cf.CONV_BF16, cf.CONV_BF16)
     assert q(W(groups=0)) == -1
-    assert q(W(padding=1, dilation=2)) == cf.VARIANT_DIRECT
+    assert q(W(padding=1, dilation=2)) == cf.VARIANT_TILED
+    assert q(W(padding=1, dilation=2), cf.CONV_F32) == cf.VARIANT_DIRECT
     dq = lambda win: lib.conv_depthwise_window_auto_variant(8, 72, 56, 56, 1, 5, 5, ctypes.byref(win))
     assert dq(W(stride=2, padding=2)) == lib.conv_depthwise_auto_variant(8, 72, 56, 56, 1, 5, 5, 2, 2, 2, 2, 1, 1)
     assert dq(W(groups=2)) == -1
