@@ -71,6 +71,8 @@ class Runner:
         self.sets = [make_set(i) for i in range(want)]
         self.launch = launch
         self.graph = None
+        self.kernels_per_launch = 1
+        self.launches_run = 0          # every launch this runner made (eager and replayed)
 
     def capture(self, reps_per_graph):
         torch = self.torch
@@ -79,6 +81,7 @@ class Runner:
         with torch.cuda.stream(s):          # warm the launch path outside capture
             for st in self.sets:
                 self.launch(st)
+        self.launches_run += len(self.sets)
         torch.cuda.current_stream().wait_stream(s)
         torch.cuda.synchronize()
         self.graph = torch.cuda.CUDAGraph()
@@ -93,8 +96,10 @@ class Runner:
         """Median ms per launch over `trials` timed regions of >= `steps` launches."""
         torch = self.torch
         replays = max(1, math.ceil(steps / self.launches_per_replay))
-        for _ in range(max(1, math.ceil(warmup / self.launches_per_replay))):
+        warm = max(1, math.ceil(warmup / self.launches_per_replay))
+        for _ in range(warm):
             self.graph.replay()
+        self.launches_run += (warm + trials * replays) * self.launches_per_replay
         torch.cuda.synchronize()
         results = []
         for _ in range(trials):
@@ -142,7 +147,8 @@ def dense_runner(work, mode, out_dtype_name, dtype_name=None):
             raise RuntimeError(f"conv2d_nhwc_fwd failed: {cf.status_str(rc)}")
 
     flops = 2.0 * work.N * Ho * Wo * work.Cout * work.KH * work.KW * work.Cin
-    return Runner(work.name, make_set, launch, set_bytes, mode), flops, set_bytes
+    name = f"{work.name} ({dt} X, {out_dtype_name} Y)"
+    return Runner(name, make_set, launch, set_bytes, mode), flops, set_bytes
 
 
 def dw_runner(work, mode, exact):
@@ -204,7 +210,9 @@ def im2col_route_runner(work, mode, pack_only=False):
             torch.matmul(cols, F2, out=Y)
 
     flops = 2.0 * M * work.Cout * K
-    return Runner(work.name + " im2col route", make_set, launch, set_bytes, mode), flops, set_bytes, M * K * 2
+    r = Runner(work.name + (" im2col packing only" if pack_only else " im2col route"), make_set, launch, set_bytes, mode)
+    r.kernels_per_launch = 1 if pack_only else 2
+    return r, flops, set_bytes, M * K * 2
 
 
 # Windowed layers (stride, padding, groups, 1D) measured beside the headline:
@@ -300,6 +308,9 @@ def measure(runner, steps, warmup, trials, reps_cap=None):
         reps = min(reps, reps_cap)
     runner.capture(reps)
     ms, n = runner.time(steps, warmup, trials)
+    # progress on stderr (the JSON line on stdout stays the only result)
+    print(f"bench: {runner.name}: {ms * 1e3:.2f} us per launch over {n} launches "
+          f"({runner.launches_run * runner.kernels_per_launch} kernel dispatches)", file=sys.stderr, flush=True)
     return ms, n
 
 
