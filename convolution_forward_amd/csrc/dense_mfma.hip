@@ -72,6 +72,8 @@ struct RowArgs {
     int H, W, Ho, Wo;
     int Cin, Cout;      // channels of one group (input, output)
     int f_ld;           // F row length: output channels of all groups
+    int gpack;          // 0, or the channels of one true group when several small
+                        // groups share a 64-channel tile (block-diagonal filter)
     int pt, pl;         // zero rows / columns before the input
     int R;              // output rows per band
     int bands_per_img;
@@ -157,10 +159,17 @@ struct FilterSlice {
 
     // o0: first output channel of the tile within its group; oc0: first
     // output channel of the group (F rows hold all groups' outputs).
+    //
+    // With small groups packed into the tile (a.gpack = G), tile input
+    // channel c and output channel o belong to true groups c / G and o / G;
+    // F holds G input channels per tap, and entries between different groups
+    // are the zeros of the block-diagonal filter (eight consecutive outputs
+    // never straddle a group: G is a multiple of 8).
     __device__ __forceinline__ void issue(const RowArgs &a, int o0, int oc0, int tid)
     {
+        const int fcin = a.gpack ? a.gpack : a.Cin;          // F rows per tap
         const __amdgpu_buffer_rsrc_t fr = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint16_t *>(a.F), 0, KH * KW * a.Cin * a.f_ld * 2, BUF_WORD3);
+            const_cast<uint16_t *>(a.F), 0, KH * KW * fcin * a.f_ld * 2, BUF_WORD3);
 #pragma unroll
         for (int t = 0; t < ITEMS; ++t) {
             const int it = tid + t * THREADS;
@@ -168,9 +177,14 @@ struct FilterSlice {
             const int c = (it >> 3) % CINP;
             const int tap = (it >> 3) / CINP;
             const int o = o0 + og * 8;
-            const bool ok = tap < KH * KW && c < a.Cin && o < a.Cout;
+            bool ok = tap < KH * KW && c < a.Cin && o < a.Cout;
+            int cf = c;
+            if (a.gpack) {
+                ok = ok && c / a.gpack == o / a.gpack;
+                cf = c % a.gpack;
+            }
             fv[t] = __builtin_amdgcn_raw_buffer_load_b128(
-                fr, ok ? (uint32_t)((((int64_t)tap * a.Cin + c) * a.f_ld + oc0 + o) * 2) : OOB, 0, 0);
+                fr, ok ? (uint32_t)((((int64_t)tap * fcin + cf) * a.f_ld + oc0 + o) * 2) : OOB, 0, 0);
         }
     }
 
@@ -697,17 +711,41 @@ DenseProblem regroup_pointwise(const DenseProblem &p)
 
 }  // namespace
 
+// Small groups (grouped convolution between dense and depthwise, "Convolution
+// Is Wx+b Moving Across a Signal", section "Find the same sum in CKE's C
+// kernels"): when every group has G = 8, 16 or 32 input and output channels,
+// 64 / G groups share one 64-channel tile with a block-diagonal filter. X is
+// then read once, in whole 128-byte pixel rows, instead of once per group in
+// G-channel slivers; the extra matrix-core work multiplies zeros.
+int pack_groups(const DenseProblem &p, DenseProblem *q)
+{
+    if (p.groups <= 1 || p.Cin != p.Cout || p.Cin % 64 != 0)
+        return 0;
+    const int g = p.Cin / p.groups;
+    if (g != 8 && g != 16 && g != 32)
+        return 0;
+    *q = p;
+    q->groups = p.Cin / 64;
+    return g;
+}
+
 bool dense_mfma_bf16_supports(const DenseProblem &p)
 {
     Plan plan;
+    DenseProblem q;
+    if (pack_groups(p, &q) && plan_rows(q, &plan))
+        return true;
     return plan_rows(regroup_pointwise(p), &plan);
 }
 
 hipError_t launch_dense_mfma_bf16(const DenseProblem &p0, hipStream_t s)
 {
-    const DenseProblem p = regroup_pointwise(p0);
     Plan plan;
-    if (!plan_rows(p, &plan))
+    DenseProblem packed;
+    const int gpack = pack_groups(p0, &packed);
+    const bool use_pack = gpack != 0 && plan_rows(packed, &plan);
+    const DenseProblem p = use_pack ? packed : regroup_pointwise(p0);
+    if (!use_pack && !plan_rows(p, &plan))
         return hipErrorNotSupported;
     RowArgs a;
     a.X = static_cast<const uint16_t *>(p.X);
@@ -727,6 +765,7 @@ hipError_t launch_dense_mfma_bf16(const DenseProblem &p0, hipStream_t s)
     a.Cin = p.Cin / p.groups;
     a.Cout = p.Cout / p.groups;
     a.f_ld = p.Cout;
+    a.gpack = use_pack ? gpack : 0;
     a.pt = p.pt;
     a.pl = p.pl;
     a.groups = p.groups;

@@ -58,6 +58,11 @@ DENSE = [  # name, (N,H,W,Cin), (KH,KW,Cout), stride, padding, dilation, groups
     ("mfma_1x1_padded", (1, 9, 10, 32), (1, 1, 40), 1, 1, 1, 1),
     ("mfma_wide_same", (1, 6, 120, 16), (3, 3, 16), 1, 1, 1, 1),
     ("mfma_pad_2_stride2", (1, 17, 9, 24), (3, 3, 8), 2, 2, 1, 1),
+    # small groups packed block-diagonally into 64-channel tiles
+    ("mfma_pack_g8_stride2", (2, 15, 18, 128), (3, 3, 128), 2, 1, 1, 16),
+    ("mfma_pack_g32_1x1", (2, 9, 10, 128), (1, 1, 128), 1, 0, 1, 4),
+    ("mfma_pack_g16_wide", (1, 7, 100, 128), (3, 3, 128), 1, 1, 1, 8),
+    ("mfma_pack_g16_ragged", (3, 5, 21, 64), (3, 3, 64), 1, (1, 0, 2, 1), 1, 4),
     # windows only the streamed-filter GEMM kernel takes
     ("gemm_3x3_cin128", (2, 14, 15, 128), (3, 3, 72), 1, 1, 1, 1),
     ("gemm_dilated", (1, 20, 18, 32), (3, 3, 40), 1, 2, 2, 1),
