@@ -249,6 +249,10 @@ __device__ __forceinline__ void bias_issue(const RowArgs &a, int o0, int oc0, in
 // S is the stride along both axes (1 or 2). A band of output rows
 // t = 0..R-1 reads input rows y0*S - pt + r for r = 0..(R-1)*S + KH - 1;
 // output row t uses rows r = t*S + i (filter row i). NR bounds that count.
+// Whether the row kernel prefetches the next row's X fragments (three LDS
+// row buffers instead of two).
+constexpr bool prefetch_rows(int KW, int CS, int BPW, int MAXC) { return BPW == 1 && MAXC == 1 && KW * CS <= 6; }
+
 template <int KH, int KW, int S>
 struct Window {
     static constexpr int INFLIGHT = (KH + S - 1) / S;    // output rows summing at once
@@ -329,8 +333,17 @@ void dense_rows_mfma(RowArgs a)
     //    above the filter loads (the counter is in order, so the filter wait
     //    would then also wait for the rows).
     __builtin_amdgcn_sched_barrier(0);
-    constexpr int DW = MAXC == 1 ? 4 : 2;    // rows of loads in flight (register budget)
+    // With one block per wave and one chunk per thread per row, the next
+    // row's X fragments are read during the current row's MFMAs: rows then
+    // rotate through three LDS buffers (row r in buffer r % 3; row r + 2 is
+    // committed during step r), and three rows of loads are in flight. With
+    // more blocks, chunks or fragments per row those registers are not there
+    // (the compiler would spill), and two buffers suffice.
+    constexpr bool PF = prefetch_rows(KW, CS, BPW, MAXC);
+    constexpr int NBUF = PF ? 3 : 2;
+    constexpr int DW = PF ? 3 : MAXC == 1 ? 4 : 2;    // rows of loads in flight (register budget)
     constexpr int D = NR < DW ? NR : DW;
+    static_assert(!PF || D >= 3, "the prefetching ring loads three rows ahead");
     u32x4 xin[D][MAXC];
 #pragma unroll
     for (int i = 0; i < D; ++i)
@@ -339,15 +352,15 @@ void dense_rows_mfma(RowArgs a)
             xin[i][k] = __builtin_amdgcn_raw_buffer_load_b128(
                 xr, chunk_off<CINP>(a, iy0 + i, tid + k * THREADS, iy_end), 0, 0);
 
-    // 3. Filter slice into LDS; 4. zero the padding slots of both row
-    //    buffers (never overwritten afterwards) and commit input row 0 into
-    //    buffer 0; 5. the A fragments into registers. With the rows apart
-    //    from the staging area, 3 and 4 share one barrier and the loop can
-    //    start right after 5; otherwise 4 waits until every wave has read its
-    //    fragments.
+    // 3. Filter slice into LDS; 4. zero the padding slots of every row
+    //    buffer (never overwritten afterwards) and commit the first input
+    //    rows (row 0, and row 1 when prefetching); 5. the A fragments into
+    //    registers. With the rows apart from the staging area, 3 and 4 share
+    //    one barrier and the loop can start right after 5; otherwise 4 waits
+    //    until every wave has read its fragments.
     auto commit_first_row = [&]() __attribute__((always_inline)) {
         const int zslots = a.row_slots - a.W;
-        for (int q = tid; q < 2 * zslots * CG; q += THREADS) {
+        for (int q = tid; q < NBUF * zslots * CG; q += THREADS) {
             const int b = q / (zslots * CG);
             const int zq = q - b * zslots * CG;
             const int zi = zq / CG;
@@ -359,6 +372,14 @@ void dense_rows_mfma(RowArgs a)
             const int q = tid + k * THREADS;
             if (q < a.chunks_per_row)
                 put_chunk<CINP, S>(rows, a.pl, q, xin[0][k]);
+        }
+        if constexpr (PF && NR > 1) {
+#pragma unroll
+            for (int k = 0; k < MAXC; ++k) {
+                const int q = tid + k * THREADS;
+                if (q < a.chunks_per_row)
+                    put_chunk<CINP, S>(rows + a.row_elems, a.pl, q, xin[1][k]);
+            }
         }
     };
     filt.commit(ft, tid);
@@ -413,6 +434,22 @@ void dense_rows_mfma(RowArgs a)
             for (int nb = 0; nb < NBW; ++nb)
                 acc[s2][qb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+    // X fragments of input row r for block qb (eight channels of one pixel
+    // per lane, for each tap column j and channel step).
+    auto read_frags = [&](const uint16_t *rowp, int qb, bf16x8 (&xb)[KW * CS]) __attribute__((always_inline)) {
+        const int x = (pg + 4 * qb) * 16 + (lane & 15);
+        const int xl = min(x, a.Wo - 1);
+#pragma unroll
+        for (int jc = 0; jc < KW * CS; ++jc) {
+            const int j = jc / CS;
+            const int cs = jc % CS;
+            xb[jc] = *reinterpret_cast<const bf16x8 *>(rowp + (xl * S + j) * PITCH + cs * 32 + (lane >> 4) * 8);
+        }
+    };
+    bf16x8 xn[KW * CS];          // prefetched fragments of the next row (PF)
+    if constexpr (PF)
+        read_frags(rows, 0, xn);
+
     static_for<0, NR>([&](auto RR) {
         constexpr int r = decltype(RR)::value;
         if constexpr (r >= 1 && Win::completes(r - 1, RMAX))
@@ -423,17 +460,22 @@ void dense_rows_mfma(RowArgs a)
                 xin[(r + D) % D][k] = __builtin_amdgcn_raw_buffer_load_b128(
                     xr, chunk_off<CINP>(a, iy0 + r + D, tid + k * THREADS, iy_end), 0, 0);
         }
-        const uint16_t *rowp = rows + (r & 1) * a.row_elems;
+        const uint16_t *rowp = rows + (r % NBUF) * a.row_elems;
 #pragma unroll
         for (int qb = 0; qb < BPW; ++qb) {
             const int x = (pg + 4 * qb) * 16 + (lane & 15);
-            const int xl = min(x, a.Wo - 1);
             bf16x8 xb[KW * CS];
+            if constexpr (PF) {
+                // Row r was read during the previous step; row r + 1 was
+                // committed then too, so its fragments can be read now,
+                // under this row's MFMAs.
 #pragma unroll
-            for (int jc = 0; jc < KW * CS; ++jc) {
-                const int j = jc / CS;
-                const int cs = jc % CS;
-                xb[jc] = *reinterpret_cast<const bf16x8 *>(rowp + (xl * S + j) * PITCH + cs * 32 + (lane >> 4) * 8);
+                for (int jc = 0; jc < KW * CS; ++jc)
+                    xb[jc] = xn[jc];
+                if constexpr (r + 1 < NR)
+                    read_frags(rows + ((r + 1) % NBUF) * a.row_elems, 0, xn);
+            } else {
+                read_frags(rowp, qb, xb);
             }
 #pragma unroll
             for (int i = 0; i < KH; ++i) {
@@ -473,16 +515,18 @@ void dense_rows_mfma(RowArgs a)
                 }
             }
         }
-        if constexpr (r + 1 < NR) {
-            // Input row r+1 into the other buffer for the next step (its
-            // previous row was last read before the barrier that ended the
-            // previous step; rows past the band are zeros and never feed a
-            // stored output).
+        // The input row committed now: r + 2 with prefetching (its buffer
+        // last held row r - 1, whose fragments were read during step r - 2),
+        // else r + 1 into the other buffer (its previous row was last read
+        // before the barrier that ended the previous step). Rows past the
+        // band are zeros and never feed a stored output.
+        constexpr int rc = PF ? r + 2 : r + 1;
+        if constexpr (rc < NR) {
 #pragma unroll
             for (int k = 0; k < MAXC; ++k) {
                 const int q = tid + k * THREADS;
                 if (q < a.chunks_per_row)
-                    put_chunk<CINP, S>(rows + ((r + 1) & 1) * a.row_elems, a.pl, q, xin[(r + 1) % D][k]);
+                    put_chunk<CINP, S>(rows + (rc % NBUF) * a.row_elems, a.pl, q, xin[rc % D][k]);
             }
         }
         __syncthreads();
@@ -596,7 +640,7 @@ bool plan_rows(const DenseProblem &p, Plan *plan)
     // fits, else [max(filter staging, two input rows)] [two output tiles].
     const size_t pitch = pl.S == 1 ? (size_t)32 * pl.CS + 16 : (size_t)32 * pl.CS + 8;
     const size_t filt = (size_t)p.KH * p.KW * 32 * pl.CS * (COUT_TILE + 8) * 2;
-    const size_t rows = (size_t)2 * pl.slots * pitch * 2;
+    const size_t rows = (size_t)(prefetch_rows(p.KW, pl.CS, pl.BPW, pl.MAXC) ? 3 : 2) * pl.slots * pitch * 2;
     const size_t otiles = 2 * (size_t)64 * pl.BPW * (COUT_TILE * yesz + 32);
     if (filt + rows + otiles <= (size_t)LDS_BYTES_MAX) {
         pl.rows_off = filt;
