@@ -208,12 +208,13 @@ struct FilterSlice {
     // consecutive input channels of one output channel, which is the
     // A-operand layout (lane holds 8 consecutive k of row o = lane % 16).
     // Two reads give the 8 channels of the lane's k-group.
+    template <int I0 = 0, int I1 = KH>
     static __device__ __forceinline__ void fragments(const uint16_t *ft, int lane, int half, bf16x8 (&wf)[KSTEPS][NBW])
     {
         const int g = lane >> 4;           // k-group: channels 8g..8g+7 of a 32-channel step
         const int r = lane & 15;
 #pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks) {
+        for (int ks = I0 * KW * CS; ks < I1 * KW * CS; ++ks) {
             const int tap = ks / CS;
             const int cs = ks % CS;
 #pragma unroll
@@ -382,16 +383,39 @@ void dense_rows_mfma(RowArgs a)
             }
         }
     };
-    filt.commit(ft, tid);
-    if (rows_apart)
-        commit_first_row();
-    __syncthreads();
+    // With the rows apart from the staging area, the staged filter stays in
+    // LDS during the loop: only filter row 0's fragments are read now, and
+    // those of filter row i at the start of step i (the first step to use
+    // them), under the first steps' few MFMAs. (With fp32 outputs or stride
+    // 2 the longer register live ranges would spill: those read them all
+    // here.)
+    constexpr bool LAZY = PF && S == 1 && OUT_BF16;
     bf16x8 wf[KSTEPS][NBW];
-    FilterSlice<KH, KW, CS>::fragments(ft, lane, half, wf);
-    if (!rows_apart) {
-        __syncthreads();      // the staging area becomes the input-row area
-        commit_first_row();
+    auto stage_eager = [&]() __attribute__((always_inline)) {
+        filt.commit(ft, tid);
+        if (rows_apart)
+            commit_first_row();
         __syncthreads();
+        FilterSlice<KH, KW, CS>::fragments(ft, lane, half, wf);
+        if (!rows_apart) {
+            __syncthreads();      // the staging area becomes the input-row area
+            commit_first_row();
+            __syncthreads();
+        }
+    };
+    bool lazy = false;
+    if constexpr (LAZY) {
+        lazy = rows_apart;
+        if (lazy) {
+            filt.commit(ft, tid);
+            commit_first_row();
+            __syncthreads();
+            FilterSlice<KH, KW, CS>::template fragments<0, 1>(ft, lane, half, wf);
+        } else {
+            stage_eager();
+        }
+    } else {
+        stage_eager();
     }
 
     // A finished output row leaves as 16-byte chunks from its LDS tile:
@@ -452,6 +476,10 @@ void dense_rows_mfma(RowArgs a)
 
     static_for<0, NR>([&](auto RR) {
         constexpr int r = decltype(RR)::value;
+        if constexpr (LAZY && r >= 1 && r < KH) {
+            if (lazy)
+                FilterSlice<KH, KW, CS>::template fragments<r, r + 1>(ft, lane, half, wf);
+        }
         if constexpr (r >= 1 && Win::completes(r - 1, RMAX))
             store_row((r - KH) / S);
         if constexpr (r + D < NR) {
