@@ -251,8 +251,13 @@ __device__ __forceinline__ void bias_issue(const RowArgs &a, int o0, int oc0, in
 // t = 0..R-1 reads input rows y0*S - pt + r for r = 0..(R-1)*S + KH - 1;
 // output row t uses rows r = t*S + i (filter row i). NR bounds that count.
 // Whether the row kernel prefetches the next row's X fragments (three LDS
-// row buffers instead of two).
-constexpr bool prefetch_rows(int KW, int CS, int BPW, int MAXC) { return BPW == 1 && MAXC == 1 && KW * CS <= 6; }
+// row buffers instead of two): one block per wave, and either one chunk per
+// thread per row with at most six fragments (the 3x3 layers, whose filter
+// fills most registers) or a 1x1 filter (whose filter registers are few).
+constexpr bool prefetch_rows(int KW, int CS, int BPW, int MAXC)
+{
+    return BPW == 1 && ((MAXC == 1 && KW * CS <= 6) || (KW == 1 && CS <= 8));
+}
 
 template <int KH, int KW, int S>
 struct Window {
@@ -334,12 +339,11 @@ void dense_rows_mfma(RowArgs a)
     //    above the filter loads (the counter is in order, so the filter wait
     //    would then also wait for the rows).
     __builtin_amdgcn_sched_barrier(0);
-    // With one block per wave and one chunk per thread per row, the next
-    // row's X fragments are read during the current row's MFMAs: rows then
-    // rotate through three LDS buffers (row r in buffer r % 3; row r + 2 is
-    // committed during step r), and three rows of loads are in flight. With
-    // more blocks, chunks or fragments per row those registers are not there
-    // (the compiler would spill), and two buffers suffice.
+    // When prefetch_rows allows it, the next row's X fragments are read
+    // during the current row's MFMAs: rows then rotate through three LDS
+    // buffers (row r in buffer r % 3; row r + 2 is committed during step r),
+    // and three rows of loads are in flight. Otherwise those registers are
+    // not there (the compiler would spill) and two buffers suffice.
     constexpr bool PF = prefetch_rows(KW, CS, BPW, MAXC);
     constexpr int NBUF = PF ? 3 : 2;
     constexpr int DW = PF ? 3 : MAXC == 1 ? 4 : 2;    // rows of loads in flight (register budget)
