@@ -809,9 +809,9 @@ bool dense_mfma_bf16_supports(const DenseProblem &p)
 {
     Plan plan;
     DenseProblem q;
-    if (pack_groups(p, &q) && plan_rows(q, &plan))
+    if (pack_groups(p, &q) && (dense_band_supports(q) || plan_rows(q, &plan)))
         return true;
-    return plan_rows(regroup_pointwise(p), &plan);
+    return dense_band_supports(p) || plan_rows(regroup_pointwise(p), &plan);
 }
 
 hipError_t launch_dense_mfma_bf16(const DenseProblem &p0, hipStream_t s)
@@ -819,6 +819,13 @@ hipError_t launch_dense_mfma_bf16(const DenseProblem &p0, hipStream_t s)
     Plan plan;
     DenseProblem packed;
     const int gpack = pack_groups(p0, &packed);
+    // Unit-stride windows with bf16 output and rows of at most 64 pixels run
+    // on the band kernel (dense_band_mfma.hip), which requests the whole
+    // band of input rows up front.
+    if (gpack != 0 && dense_band_supports(packed))
+        return launch_dense_band(packed, gpack, s);
+    if (dense_band_supports(p0))
+        return launch_dense_band(p0, 0, s);
     const bool use_pack = gpack != 0 && plan_rows(packed, &plan);
     const DenseProblem p = use_pack ? packed : regroup_pointwise(p0);
     if (!use_pack && !plan_rows(p, &plan))
