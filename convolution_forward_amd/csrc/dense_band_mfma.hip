@@ -140,7 +140,7 @@ __device__ __forceinline__ void static_for(Fn &&fn)
     }
 }
 
-template <int KH, int KW, int CS, int NR, int ORDER = 0>
+template <int KH, int KW, int CS, int NR, int ORDER = 0, int LS = KH - 1>
 struct BandShape {
     static constexpr int CINP = 32 * CS;
     static constexpr int CG = CINP / 8;                     // 16-byte units per pixel
@@ -152,7 +152,8 @@ struct BandShape {
     static constexpr int RMAX = NR - KH + 1;                // output rows a band holds
     static constexpr int EARLY = NR < 3 ? NR : 3;           // input rows requested before filter rows 1..KH-1
     static constexpr int OSTORE = 1;                        // store instructions per output row and wave
-    static constexpr int LAST_SYNC = NR - 1 < KH - 1 ? NR - 1 : KH - 1;  // last step that ends with a barrier
+    static constexpr int LAST_SYNC = LS;                    // last step that ends with a barrier
+    static_assert(LS >= KH - 1 && LS + 2 < NR, "filter rows are staged at barriers; rows past LS + 1 exist");
     static constexpr size_t LDS = (size_t)2 * FROW * 2 + (size_t)NR * ROW_BYTES + (BT / 64) * 16 * OP_PITCH;
 
     // Output rows stored by the end of step r: row t completes (and is
@@ -240,11 +241,11 @@ __device__ __forceinline__ void tr_reads(uint32_t base, i16x4 (&p)[B::TRN])
 
 #undef CF_TR
 
-template <int KH, int KW, int CS, int NR, int SAUX, int ORDER>
+template <int KH, int KW, int CS, int NR, int SAUX, int ORDER, int LS>
 __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void dense_band_mfma(BandArgs a)
 {
-    using B = BandShape<KH, KW, CS, NR, ORDER>;
+    using B = BandShape<KH, KW, CS, NR, ORDER, LS>;
     constexpr int CINP = B::CINP;
     constexpr int CG = B::CG;
     constexpr int KSR = B::KSR;
@@ -531,11 +532,11 @@ void dense_band_mfma(BandArgs a)
     });
 }
 
-template <int KH, int KW, int CS, int NR, int SAUX = 16, int ORDER = 1>
+template <int KH, int KW, int CS, int NR, int SAUX = 16, int ORDER = 1, int LS = KH - 1>
 hipError_t launch_band(const BandArgs &a, dim3 grid, hipStream_t s)
 {
-    auto kern = dense_band_mfma<KH, KW, CS, NR, SAUX, ORDER>;
-    constexpr size_t lds = BandShape<KH, KW, CS, NR, ORDER>::LDS;
+    auto kern = dense_band_mfma<KH, KW, CS, NR, SAUX, ORDER, LS>;
+    constexpr size_t lds = BandShape<KH, KW, CS, NR, ORDER, LS>::LDS;
     static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (attr != hipSuccess)
