@@ -40,8 +40,8 @@ COLD_BYTES = 1 << 30             # rotate at least this much distinct memory in 
 # the same counter reads for the plain copy kernel of known size. The file
 # records the hash of the kernel source it was taken on; once the source
 # changes the figure no longer describes the kernel and is reported as null.
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "dense_rows_mfma_dense3x3_bf16_traffic.txt")
-HEADLINE_SOURCE = os.path.join(ROOT, "convolution_forward_amd", "csrc", "dense_mfma.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "dense_band_mfma_dense3x3_bf16_traffic.txt")
+HEADLINE_SOURCE = os.path.join(ROOT, "convolution_forward_amd", "csrc", "dense_band_mfma.hip")
 
 
 def parse():
