@@ -22,12 +22,14 @@
 //    commit instructions); rows arrive in order and each step waits only
 //    for the row it is about to read;
 //  * the filter slice is requested one filter row (K taps) at a time: row 0
-//    first, then the first input rows, then the other filter rows, then the
-//    rest of the input. The first step needs only filter row 0 and input
-//    rows 0-1, so the matrix cores start after about a third of the filter
-//    has arrived instead of all of it. Filter row i is staged in LDS at
-//    step i - 1 and read into registers (gfx950 transpose read) at step i;
-//    two staging areas alternate.
+//    and input rows 0-1 first (a barrier then makes every wave put these in
+//    the memory pipeline before any wave asks for more), then input row 2
+//    and the other filter rows, and the rest of the input at the start of
+//    step 0. The first step needs only filter row 0 and input rows 0-1, so
+//    the matrix cores start after about a third of the filter has arrived
+//    instead of all of it. Filter row i is staged in LDS at step i - 1 and
+//    read into registers (gfx950 transpose read) at step i; two staging
+//    areas alternate.
 //
 // Work decomposition (one workgroup = 8 waves = 512 threads, 2 per SIMD):
 //  * Wave w keeps the 32-channel half (w & 1) of the tile's filter as A
@@ -168,11 +170,17 @@ struct BandShape {
     // 0: bias, filter row 0, input rows 0..EARLY-1, filter rows 1..KH-1,
     // the other input rows. Order 1: the same, but the other input rows
     // only at the start of step 0. Order 2: input rows 0 and 1 first, then
-    // bias and filter row 0, then as order 0.
+    // bias and filter row 0, then as order 0. Order 3: as order 1, with
+    // filter rows 1..KH-1 also issued at the start of step 0 (before the
+    // other input rows). Order 4: as order 1, with a barrier after input
+    // row 1, so that every wave's first loads reach the memory pipeline
+    // before any wave's later ones.
     static constexpr int after_row(int q, int r)
     {
+        if (ORDER == 3 && r < 0)
+            return EARLY - 1 - q;                           // only the early rows are out
         int n = NR - 1 - q;                                 // later rows
-        if (ORDER == 1 && r < 0)
+        if ((ORDER == 1 || ORDER == 3 || ORDER == 4) && r < 0)
             n -= NR - EARLY;                                // not issued yet
         if (q < EARLY)
             n += FITEMS * (KH - 1);                         // filter rows 1..KH-1
@@ -292,39 +300,37 @@ void dense_band_mfma(BandArgs a)
     const __amdgpu_buffer_rsrc_t fr = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t *>(a.F), 0, KH * KW * fcin * a.f_ld * 2, BUF_WORD3);
 
-    // Filter row i: load item it -> (8-output group og fastest, then input
-    // channel c, then tap j), eight lanes per 128-byte row of F. With small
-    // groups packed into the tile (gpack = G), entries between different
-    // true groups are the zeros of the block-diagonal filter.
+    // Filter row i: load item it = tid + t*BT -> (8-output group og
+    // fastest, then input channel c, then tap column j), eight lanes per
+    // 128-byte row of F. Everything but the tap is fixed per thread: item t
+    // reads tap column fj0 + t*JSTEP, channel fc, outputs o0 + 8*(tid & 7).
+    // With small groups packed into the tile (gpack = G), entries between
+    // different true groups are the zeros of the block-diagonal filter.
+    constexpr int JSTEP = (BT / 8) / CINP;
+    static_assert(JSTEP >= 1 && (BT / 8) % CINP == 0, "an item round covers whole taps");
+    const int fog = tid & 7;
+    const int fc = (tid >> 3) % CINP;
+    const int fj0 = (tid >> 3) / CINP;
+    const int fo = o0 + fog * 8;
+    const bool fok = fc < a.Cin && fo < a.Cout && (a.gpack == 0 || fc / a.gpack == fo / a.gpack);
+    const uint32_t fgoff = (uint32_t)(((a.gpack ? fc % a.gpack : fc) * a.f_ld + oc0 + fo) * 2);
+    const uint32_t ftap = (uint32_t)(fcin * a.f_ld * 2);      // bytes per tap
     u32x4 fv[KH][B::FITEMS];
     auto issue_frow = [&](const int i) __attribute__((always_inline)) {
 #pragma unroll
         for (int t = 0; t < B::FITEMS; ++t) {
-            const int it = tid + t * BT;
-            const int og = it & 7;
-            const int c = (it >> 3) % CINP;
-            const int j = (it >> 3) / CINP;
-            const int o = o0 + og * 8;
-            bool ok = j < KW && c < a.Cin && o < a.Cout;
-            int cf = c;
-            if (a.gpack) {
-                ok = ok && c / a.gpack == o / a.gpack;
-                cf = c % a.gpack;
-            }
+            const int j = fj0 + t * JSTEP;
             fv[i][t] = __builtin_amdgcn_raw_buffer_load_b128(
-                fr, ok ? (uint32_t)((((int64_t)(i * KW + j) * fcin + cf) * a.f_ld + oc0 + o) * 2) : OOB, 0, 0);
+                fr, (fok && j < KW) ? fgoff + (uint32_t)(i * KW + j) * ftap : OOB, 0, 0);
         }
     };
     auto commit_frow = [&](const int i) __attribute__((always_inline)) {
         uint16_t *ft = farea + (i & 1) * B::FROW;
 #pragma unroll
         for (int t = 0; t < B::FITEMS; ++t) {
-            const int it = tid + t * BT;
-            const int og = it & 7;
-            const int c = (it >> 3) % CINP;
-            const int j = (it >> 3) / CINP;
+            const int j = fj0 + t * JSTEP;
             if (j < KW)
-                *reinterpret_cast<u32x4 *>(ft + (j * CINP + c) * FPITCH + og * 8) = fv[i][t];
+                *reinterpret_cast<u32x4 *>(ft + (j * CINP + fc) * FPITCH + fog * 8) = fv[i][t];
         }
     };
     // A fragments of filter row i (k-steps i*KSR ..). Within each 16-lane
@@ -391,6 +397,14 @@ void dense_band_mfma(BandArgs a)
         issue_frow(0);
         __builtin_amdgcn_sched_barrier(0);
         static_for<2, B::EARLY>([&](auto R) { dma_row(decltype(R)::value); });
+    } else if constexpr (ORDER == 4) {
+        issue_bias();
+        issue_frow(0);
+        __builtin_amdgcn_sched_barrier(0);
+        static_for<0, 2>([&](auto R) { dma_row(decltype(R)::value); });
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_barrier" ::: "memory");
+        static_for<2, B::EARLY>([&](auto R) { dma_row(decltype(R)::value); });
     } else {
         issue_bias();
         issue_frow(0);
@@ -398,9 +412,10 @@ void dense_band_mfma(BandArgs a)
         static_for<0, B::EARLY>([&](auto R) { dma_row(decltype(R)::value); });
     }
     __builtin_amdgcn_sched_barrier(0);
-    static_for<1, KH>([&](auto I) { issue_frow(decltype(I)::value); });
+    if constexpr (ORDER != 3)
+        static_for<1, KH>([&](auto I) { issue_frow(decltype(I)::value); });
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (ORDER != 1)
+    if constexpr (ORDER == 0 || ORDER == 2)
         static_for<B::EARLY, NR>([&](auto R) { dma_row(decltype(R)::value); });
     __builtin_amdgcn_sched_barrier(0);
 
@@ -461,8 +476,10 @@ void dense_band_mfma(BandArgs a)
     // steps need no barrier at all and the waves run freely to the end.
     static_for<0, NR>([&](auto RR) {
         constexpr int r = decltype(RR)::value;
-        if constexpr (ORDER == 1 && r == 0) {
+        if constexpr ((ORDER == 1 || ORDER == 3 || ORDER == 4) && r == 0) {
             __builtin_amdgcn_sched_barrier(0);
+            if constexpr (ORDER == 3)
+                static_for<1, KH>([&](auto I) { issue_frow(decltype(I)::value); });
             static_for<B::EARLY, NR>([&](auto R) { dma_row(decltype(R)::value); });
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -532,7 +549,7 @@ void dense_band_mfma(BandArgs a)
     });
 }
 
-template <int KH, int KW, int CS, int NR, int SAUX = 16, int ORDER = 1, int LS = KH - 1>
+template <int KH, int KW, int CS, int NR, int SAUX = 16, int ORDER = 4, int LS = KH - 1>
 hipError_t launch_band(const BandArgs &a, dim3 grid, hipStream_t s)
 {
     auto kern = dense_band_mfma<KH, KW, CS, NR, SAUX, ORDER, LS>;
