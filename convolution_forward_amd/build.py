@@ -37,6 +37,7 @@ COMMON_FLAGS = [
 EXTRA_FLAGS = {
     "depthwise_direct.hip": ["-ffp-contract=off"],
     "depthwise_tiled.hip": ["-ffp-contract=off"],
+    "depthwise_pad.hip": ["-ffp-contract=off"],
 }
 
 

@@ -58,6 +58,8 @@ hipError_t launch_dense_mfma_f32(const DenseProblem &p, hipStream_t s);
 // Depthwise kernels.
 hipError_t launch_dw_direct(const DwProblem &p, hipStream_t s);
 bool dw_tiled_supports(const DwProblem &p);
+bool dw_pad_supports(const DwProblem &p);
+hipError_t launch_dw_pad(const DwProblem &p, hipStream_t s);
 hipError_t launch_dw_tiled(const DwProblem &p, hipStream_t s);
 
 // A validated explicit patch-matrix problem: NHWC X with element strides,
