@@ -43,7 +43,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int THREADS = 256;
-constexpr int BATCH = 8;              // loads in flight per thread per copy round
 constexpr int PL = 4;                 // padded columns before the image (>= pw)
 constexpr uint32_t OOB = 0x80000000u;
 constexpr int BUF_WORD3 = 0x00020000;
@@ -84,7 +83,10 @@ struct PadArgs {
     FastDiv div_bands, div_tpp, div_wo, div_cpr, div_rows;  // div_rows: rows copied per whole plane
 };
 
-template <int KH, int KW, int S, int RT, int EXACT>
+// BATCH: 16-byte loads in flight per thread per copy round. Four cover
+// every tile of up to 1024 pieces in one round; larger tiles take eight
+// (fewer rounds) at the price of registers, i.e. of resident workgroups.
+template <int KH, int KW, int S, int RT, int BATCH, int EXACT>
 __global__ __launch_bounds__(THREADS) void dw_pad_kernel(PadArgs a)
 {
 #pragma clang fp contract(off)
@@ -211,7 +213,7 @@ __global__ __launch_bounds__(THREADS) void dw_pad_kernel(PadArgs a)
 // --- host side -------------------------------------------------------------
 
 struct PadPlan {
-    int RT, PPW, bands, RB, TPP, WP, RP, PS, tile_elems;
+    int RT, PPW, bands, RB, TPP, WP, RP, PS, tile_elems, batch;
     double score;
 };
 
@@ -247,6 +249,9 @@ PadPlan pad_plan_for(const DwProblem &p, int RT)
     while (t.PPW > 1 && lds_for(t.PPW) * 4 > LDS_LIMIT)
         --t.PPW;
     t.tile_elems = (int)((lds_for(t.PPW) + 3) / 4 * 4);
+    // 16-byte pieces of the largest tile: its planes, or its band's rows.
+    const int64_t rows = t.PPW > 1 ? std::min<int64_t>(p.H, t.RP - p.ph) : std::min<int64_t>(p.H, t.RP);
+    t.batch = (int64_t)t.PPW * rows * (p.W / 4) <= 4 * THREADS ? 4 : 8;
     const int64_t planes = (int64_t)p.N * p.C;
     const int64_t tiles = (planes + t.PPW - 1) / t.PPW * t.bands;
     const double slots = (double)tiles * THREADS * RT;
@@ -286,23 +291,30 @@ bool pad_plan(const DwProblem &p, PadPlan &out)
     return have;
 }
 
-template <int KH, int KW, int S, int RT>
-hipError_t launch_pad_rt(const PadArgs &a, unsigned grid, size_t lds, bool exact, hipStream_t s)
+template <int KH, int KW, int S, int RT, int BATCH>
+hipError_t launch_pad_b(const PadArgs &a, unsigned grid, size_t lds, bool exact, hipStream_t s)
 {
     if (exact)
-        hipLaunchKernelGGL((dw_pad_kernel<KH, KW, S, RT, 1>), dim3(grid), dim3(THREADS), lds, s, a);
+        hipLaunchKernelGGL((dw_pad_kernel<KH, KW, S, RT, BATCH, 1>), dim3(grid), dim3(THREADS), lds, s, a);
     else
-        hipLaunchKernelGGL((dw_pad_kernel<KH, KW, S, RT, 0>), dim3(grid), dim3(THREADS), lds, s, a);
+        hipLaunchKernelGGL((dw_pad_kernel<KH, KW, S, RT, BATCH, 0>), dim3(grid), dim3(THREADS), lds, s, a);
     return hipGetLastError();
+}
+
+template <int KH, int KW, int S, int RT>
+hipError_t launch_pad_rt(const PadArgs &a, int batch, unsigned grid, size_t lds, bool exact, hipStream_t s)
+{
+    return batch == 4 ? launch_pad_b<KH, KW, S, RT, 4>(a, grid, lds, exact, s)
+                      : launch_pad_b<KH, KW, S, RT, 8>(a, grid, lds, exact, s);
 }
 
 template <int KH, int KW, int S>
 hipError_t launch_pad_s(const PadArgs &a, const PadPlan &t, unsigned grid, size_t lds, bool exact, hipStream_t s)
 {
     switch (t.RT) {
-    case 2: return launch_pad_rt<KH, KW, S, 2>(a, grid, lds, exact, s);
-    case 4: return launch_pad_rt<KH, KW, S, 4>(a, grid, lds, exact, s);
-    default: return launch_pad_rt<KH, KW, S, 7>(a, grid, lds, exact, s);
+    case 2: return launch_pad_rt<KH, KW, S, 2>(a, t.batch, grid, lds, exact, s);
+    case 4: return launch_pad_rt<KH, KW, S, 4>(a, t.batch, grid, lds, exact, s);
+    default: return launch_pad_rt<KH, KW, S, 7>(a, t.batch, grid, lds, exact, s);
     }
 }
 
