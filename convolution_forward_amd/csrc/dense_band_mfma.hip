@@ -1,4 +1,4 @@
-// Dense NHWC cross-correlation, unit stride, bf16 operands and bf16 output:
+// Dense NHWC cross-correlation, unit stride, bf16 operands, bf16 or fp32 output:
 // an implicit GEMM on CDNA4 matrix cores whose whole band of input rows is
 // requested from memory at the start and lands in LDS without passing
 // through registers.
@@ -98,7 +98,7 @@ struct BandArgs {
     const uint16_t *X;
     const uint16_t *F;
     const float *bias;
-    uint16_t *Y;
+    void *Y;            // bf16 or fp32 (the kernel's OUT_BF16)
     int64_t xs0, xs1, xs2, ys0, ys1, ys2;
     int H, W, Ho, Wo;
     int Cin, Cout;      // channels of one group (input, output)
@@ -142,7 +142,7 @@ __device__ __forceinline__ void static_for(Fn &&fn)
     }
 }
 
-template <int KH, int KW, int CS, int NR, int ORDER = 0, int LS = KH - 1>
+template <int KH, int KW, int CS, int NR, int ORDER = 0, int LS = KH - 1, bool OUT_BF16 = true>
 struct BandShape {
     static constexpr int CINP = 32 * CS;
     static constexpr int CG = CINP / 8;                     // 16-byte units per pixel
@@ -153,7 +153,7 @@ struct BandShape {
     static constexpr int TRN = KSR * NBW * 2;               // transposed reads per filter row
     static constexpr int RMAX = NR - KH + 1;                // output rows a band holds
     static constexpr int EARLY = NR < 3 ? NR : 3;           // input rows requested before filter rows 1..KH-1
-    static constexpr int OSTORE = 1;                        // store instructions per output row and wave
+    static constexpr int OSTORE = OUT_BF16 ? 1 : NBW;       // store instructions per output row and wave
     static constexpr int LAST_SYNC = LS;                    // last step that ends with a barrier
     static_assert(LS >= KH - 1 && LS + 2 < NR, "filter rows are staged at barriers; rows past LS + 1 exist");
     static constexpr size_t LDS = (size_t)2 * FROW * 2 + (size_t)NR * ROW_BYTES + (BT / 64) * 16 * OP_PITCH;
@@ -249,11 +249,12 @@ __device__ __forceinline__ void tr_reads(uint32_t base, i16x4 (&p)[B::TRN])
 
 #undef CF_TR
 
-template <int KH, int KW, int CS, int NR, int SAUX, int ORDER, int LS>
+template <int KH, int KW, int CS, int NR, int SAUX, int ORDER, int LS, bool OUT_BF16>
 __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void dense_band_mfma(BandArgs a)
 {
-    using B = BandShape<KH, KW, CS, NR, ORDER, LS>;
+    using B = BandShape<KH, KW, CS, NR, ORDER, LS, OUT_BF16>;
+    constexpr int ESZ = OUT_BF16 ? 2 : 4;
     constexpr int CINP = B::CINP;
     constexpr int CG = B::CG;
     constexpr int KSR = B::KSR;
@@ -295,7 +296,7 @@ void dense_band_mfma(BandArgs a)
     const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t *>(a.X + (int64_t)n * a.xs0 + xc0), 0, (int)(a.x_records - xc0 * 2), BUF_WORD3);
     const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(
-        a.Y + (int64_t)n * a.ys0 + oc0, 0, (int)(a.y_records - oc0 * 2), BUF_WORD3);
+        static_cast<char *>(a.Y) + ((int64_t)n * a.ys0 + oc0) * ESZ, 0, (int)(a.y_records - oc0 * ESZ), BUF_WORD3);
     const int fcin = a.gpack ? a.gpack : a.Cin;        // F rows per tap
     const __amdgpu_buffer_rsrc_t fr = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t *>(a.F), 0, KH * KW * fcin * a.f_ld * 2, BUF_WORD3);
@@ -517,7 +518,27 @@ void dense_band_mfma(BandArgs a)
         }
         if constexpr (r + 1 < KH)
             commit_frow(r + 1);
-        if constexpr (r >= KH - 1 && r - (KH - 1) < RMAX) {
+        if constexpr (r >= KH - 1 && r - (KH - 1) < RMAX && !OUT_BF16) {
+            // Output row t is complete: the lane holds channels
+            // 32*half + 16*nb + 4*(lane/16) + {0..3} of pixel x, 16 bytes in
+            // fp32; the four lanes of a pixel write one 64-byte run.
+            constexpr int t = r - (KH - 1);
+            const int yo = y0 + t;
+#pragma unroll
+            for (int nb = 0; nb < NBW; ++nb) {
+                const f32x4 v = acc[t % KH][nb];
+                const u32x4 w = {__float_as_uint(v[0] + __uint_as_float(bq[nb][0])),
+                                 __float_as_uint(v[1] + __uint_as_float(bq[nb][1])),
+                                 __float_as_uint(v[2] + __uint_as_float(bq[nb][2])),
+                                 __float_as_uint(v[3] + __uint_as_float(bq[nb][3]))};
+                const int ch = o0 + half * 32 + nb * 16 + (lane >> 4) * 4;
+                const bool ok = x < a.Wo && ch < a.Cout && yo < y1;
+                const uint32_t off = ok ? (uint32_t)(((int64_t)yo * a.ys1 + (int64_t)x * a.ys2 + ch) * 4) : OOB;
+                __builtin_amdgcn_raw_buffer_store_b128(w, yr, off, 0, SAUX);
+                acc[t % KH][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+        }
+        if constexpr (r >= KH - 1 && r - (KH - 1) < RMAX && OUT_BF16) {
             // Output row t is complete: the lane holds channels
             // 32*half + 16*nb + 4*(lane/16) + {0..3} of pixel x. The wave
             // regroups its 16 pixels x 32 channels through its own LDS
@@ -549,11 +570,11 @@ void dense_band_mfma(BandArgs a)
     });
 }
 
-template <int KH, int KW, int CS, int NR, int SAUX = 16, int ORDER = 4, int LS = KH - 1>
+template <int KH, int KW, int CS, int NR, bool OB, int SAUX = 16, int ORDER = 4, int LS = KH - 1>
 hipError_t launch_band(const BandArgs &a, dim3 grid, hipStream_t s)
 {
-    auto kern = dense_band_mfma<KH, KW, CS, NR, SAUX, ORDER, LS>;
-    constexpr size_t lds = BandShape<KH, KW, CS, NR, ORDER, LS>::LDS;
+    auto kern = dense_band_mfma<KH, KW, CS, NR, SAUX, ORDER, LS, OB>;
+    constexpr size_t lds = BandShape<KH, KW, CS, NR, ORDER, LS, OB>::LDS;
     static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (attr != hipSuccess)
@@ -570,8 +591,9 @@ struct BandPlan {
 
 bool plan_band(const DenseProblem &p, BandPlan *plan)
 {
-    if (p.xdt != CONV_BF16 || p.ydt != CONV_BF16)
+    if (p.xdt != CONV_BF16)
         return false;
+    const int yesz = p.ydt == CONV_BF16 ? 2 : 4;
     if (p.sh != 1 || p.sw != 1 || p.dh != 1 || p.dw != 1)
         return false;
     if (p.KH != 3 || p.KW != 3)
@@ -583,13 +605,16 @@ bool plan_band(const DenseProblem &p, BandPlan *plan)
         return false;
     if ((uintptr_t)p.F % 16 != 0 || (int64_t)p.KH * p.KW * cin_g * p.Cout * 2 >= (int64_t(1) << 31))
         return false;
-    if ((uintptr_t)p.Y % 16 != 0 || p.ys[0] % 8 != 0 || p.ys[1] % 8 != 0 || p.ys[2] % 8 != 0)
+    // Output pieces are 16 bytes: 8 bf16 or 4 fp32 channels.
+    const int yvec = 16 / yesz;
+    if ((uintptr_t)p.Y % 16 != 0 || p.ys[0] % yvec != 0 || p.ys[1] % yvec != 0 || p.ys[2] % yvec != 0)
         return false;
     // Buffer offsets are 32-bit: one image of X and of Y must stay below 2 GB.
-    auto extent = [](const int64_t *s, int rows, int cols, int ch) {
-        return ((int64_t)(rows - 1) * s[1] + (int64_t)(cols - 1) * s[2] + ch) * 2;
+    auto extent = [](const int64_t *s, int rows, int cols, int ch, int esz) {
+        return ((int64_t)(rows - 1) * s[1] + (int64_t)(cols - 1) * s[2] + ch) * esz;
     };
-    if (extent(p.xs, p.H, p.W, p.Cin) >= (int64_t(1) << 31) || extent(p.ys, p.Ho, p.Wo, p.Cout) >= (int64_t(1) << 31))
+    if (extent(p.xs, p.H, p.W, p.Cin, 2) >= (int64_t(1) << 31) ||
+        extent(p.ys, p.Ho, p.Wo, p.Cout, yesz) >= (int64_t(1) << 31))
         return false;
     if (p.Wo > 64)
         return false;
@@ -626,7 +651,7 @@ hipError_t launch_dense_band(const DenseProblem &p, int gpack, hipStream_t s)
     a.X = static_cast<const uint16_t *>(p.X);
     a.F = static_cast<const uint16_t *>(p.F);
     a.bias = p.bias;
-    a.Y = static_cast<uint16_t *>(p.Y);
+    a.Y = p.Y;
     a.xs0 = p.xs[0];
     a.xs1 = p.xs[1];
     a.xs2 = p.xs[2];
@@ -650,12 +675,17 @@ hipError_t launch_dense_band(const DenseProblem &p, int gpack, hipStream_t s)
     a.groups = p.groups;
     a.row_slots = plan.slots;
     a.x_records = (uint32_t)(((int64_t)(p.H - 1) * p.xs[1] + (int64_t)(p.W - 1) * p.xs[2] + p.Cin) * 2);
-    a.y_records = (uint32_t)(((int64_t)(p.Ho - 1) * p.ys[1] + (int64_t)(p.Wo - 1) * p.ys[2] + p.Cout) * 2);
+    const int yesz = p.ydt == CONV_BF16 ? 2 : 4;
+    a.y_records = (uint32_t)(((int64_t)(p.Ho - 1) * p.ys[1] + (int64_t)(p.Wo - 1) * p.ys[2] + p.Cout) * yesz);
     const int64_t slots = (int64_t)((a.bands + 7) / 8 * 8) * a.tiles * a.groups;
     if (slots >= (int64_t(1) << 31))
         return hipErrorNotSupported;
     const dim3 grid((unsigned)slots);
-    return plan.CS == 1 ? launch_band<3, 3, 1, BAND_NR>(a, grid, s) : launch_band<3, 3, 2, BAND_NR>(a, grid, s);
+    if (p.ydt == CONV_BF16)
+        return plan.CS == 1 ? launch_band<3, 3, 1, BAND_NR, true>(a, grid, s)
+                            : launch_band<3, 3, 2, BAND_NR, true>(a, grid, s);
+    return plan.CS == 1 ? launch_band<3, 3, 1, BAND_NR, false>(a, grid, s)
+                        : launch_band<3, 3, 2, BAND_NR, false>(a, grid, s);
 }
 
 }  // namespace convfwd
