@@ -816,7 +816,7 @@ bool dense_mfma_bf16_supports(const DenseProblem &p)
     DenseProblem q;
     if (pack_groups(p, &q) && (dense_band_supports(q) || plan_rows(q, &plan)))
         return true;
-    return dense_band_supports(p) || plan_rows(regroup_pointwise(p), &plan);
+    return dense_pw_supports(p) || dense_band_supports(p) || plan_rows(regroup_pointwise(p), &plan);
 }
 
 hipError_t launch_dense_mfma_bf16(const DenseProblem &p0, hipStream_t s)
@@ -831,6 +831,10 @@ hipError_t launch_dense_mfma_bf16(const DenseProblem &p0, hipStream_t s)
         return launch_dense_band(packed, gpack, s);
     if (dense_band_supports(p0))
         return launch_dense_band(p0, 0, s);
+    // Pointwise layers whose pixels sit at one stride: the GEMM kernel
+    // (dense_pw_mfma.hip).
+    if (dense_pw_supports(p0))
+        return launch_dense_pw(p0, s);
     const bool use_pack = gpack != 0 && plan_rows(packed, &plan);
     const DenseProblem p = use_pack ? packed : regroup_pointwise(p0);
     if (!use_pack && !plan_rows(p, &plan))

@@ -47,6 +47,8 @@ struct DwProblem {
 // Dense kernels.
 hipError_t launch_dense_direct(const DenseProblem &p, hipStream_t s);
 bool dense_band_supports(const DenseProblem &p);
+bool dense_pw_supports(const DenseProblem &p);
+hipError_t launch_dense_pw(const DenseProblem &p, hipStream_t s);
 hipError_t launch_dense_band(const DenseProblem &p, int gpack, hipStream_t s);
 bool dense_mfma_bf16_supports(const DenseProblem &p);
 hipError_t launch_dense_mfma_bf16(const DenseProblem &p, hipStream_t s);
