@@ -121,7 +121,7 @@ __device__ __forceinline__ void tr16(uint32_t base, i16x4 (&p)[16])
 }
 #undef CF_TR
 
-template <int CS, bool OUT_BF16, int SLOTS>
+template <int CS, bool OUT_BF16, int SLOTS, bool FFIRST>
 struct PwShape {
     static constexpr int CINP = 32 * CS;
     static constexpr int CG = CINP / 8;                          // 16-byte units per pixel
@@ -142,18 +142,20 @@ struct PwShape {
     static_assert(FITEMS * PT == STAGE * (CT / 8), "whole filter loads per thread");
     static_assert(LDS <= (size_t)LDS_MAX, "LDS");
     // Memory instructions issued after round k's loads, at round k's wait,
-    // counted over the issue order: bias, filter stage 0, rounds
-    // 0..SLOTS-2, the other filter stages; then per round j: wait,
-    // barrier, the loads of round j + SLOTS - 1, stores.
+    // counted over the issue order: bias, the filter stages (FFIRST) or
+    // filter stage 0 only, rounds 0..SLOTS-2, the other filter stages
+    // (!FFIRST); then per round j: wait, barrier, the loads of round
+    // j + SLOTS - 1, stores.
     static constexpr int after_round(int k)
     {
-        int pos = NBIAS + FITEMS, last = -1;
+        int pos = NBIAS + FITEMS * (FFIRST ? NSTAGE : 1), last = -1;
         for (int r = 0; r <= SLOTS - 2; ++r) {
             pos += DMA;
             if (r == k)
                 last = pos;
         }
-        pos += FITEMS * (NSTAGE - 1);
+        if (!FFIRST)
+            pos += FITEMS * (NSTAGE - 1);
         for (int j = 0; j < k; ++j) {
             pos += DMA;
             if (j + SLOTS - 1 == k)
@@ -164,11 +166,11 @@ struct PwShape {
     }
 };
 
-template <int CS, int ROUNDS, bool OUT_BF16, int SLOTS>
+template <int CS, int ROUNDS, bool OUT_BF16, int SLOTS, bool FFIRST>
 __global__ __launch_bounds__(PT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void dense_pw_mfma(PwArgs a)
 {
-    using B = PwShape<CS, OUT_BF16, SLOTS>;
+    using B = PwShape<CS, OUT_BF16, SLOTS, FFIRST>;
     constexpr int CINP = B::CINP;
     constexpr int CG = B::CG;
     extern __shared__ __align__(16) uint8_t smem[];
@@ -252,15 +254,18 @@ void dense_pw_mfma(PwArgs a)
         }
     };
 
-    // Issue order (the waits depend on it): filter stage 0, the first
-    // rounds (input from HBM, the long pole), then the other filter stages
-    // (shared by every workgroup of the XCD, so mostly L2 hits). Measured:
-    // the whole filter first is 4 % slower.
+    // Issue order (the waits depend on it): the filter (shared by every
+    // workgroup of the XCD, so mostly L2 hits), then the first rounds. With
+    // the second filter half behind the rounds instead, the filter commit
+    // waits for the rounds (in-order counter) and the layer takes 1 % longer.
     issue_fstage(0);
+    if constexpr (FFIRST)
+        static_for<1, B::NSTAGE>([&](auto H) { issue_fstage(decltype(H)::value); });
     __builtin_amdgcn_sched_barrier(0);
     static_for<0, SLOTS - 1>([&](auto R) { dma_round(decltype(R)::value); });
     __builtin_amdgcn_sched_barrier(0);
-    static_for<1, B::NSTAGE>([&](auto H) { issue_fstage(decltype(H)::value); });
+    if constexpr (!FFIRST)
+        static_for<1, B::NSTAGE>([&](auto H) { issue_fstage(decltype(H)::value); });
     __builtin_amdgcn_sched_barrier(0);
 
     // A fragments: wf[k-step][nb], 8 consecutive input channels of one
@@ -376,11 +381,11 @@ void dense_pw_mfma(PwArgs a)
     });
 }
 
-template <int CS, int ROUNDS, bool OB, int SLOTS = 3>
+template <int CS, int ROUNDS, bool OB, int SLOTS = 3, bool FFIRST = true>
 hipError_t launch_pw(const PwArgs &a, dim3 grid, hipStream_t s)
 {
-    auto kern = dense_pw_mfma<CS, ROUNDS, OB, SLOTS>;
-    constexpr size_t lds = PwShape<CS, OB, SLOTS>::LDS;
+    auto kern = dense_pw_mfma<CS, ROUNDS, OB, SLOTS, FFIRST>;
+    constexpr size_t lds = PwShape<CS, OB, SLOTS, FFIRST>::LDS;
     static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (attr != hipSuccess)

@@ -154,3 +154,46 @@ def test_gpu_dw_padded_kernel_coverage_and_repeat():
     assert not torch.isnan(y1).any()
     y2 = _dw(X, w, None, 1, 2, "fast")
     assert torch.equal(y1.view(torch.int32), y2.view(torch.int32))
+
+
+# --- pointwise (1x1) GEMM kernel ------------------------------------------------
+
+POINTWISE = [  # N, H, W, Cin, Cout, out dtype, bias, pixel stride of X (None: contiguous)
+    (2, 7, 11, 256, 136, torch.bfloat16, False, None),   # 154 pixels: a ragged last block, a partial channel tile
+    (4, 10, 13, 256, 512, torch.bfloat16, True, None),   # four channel tiles, bias
+    (1, 5, 9, 128, 64, torch.bfloat16, False, None),     # two 32-channel steps per filter half
+    (2, 7, 11, 256, 136, torch.float32, True, None),     # fp32 output straight from the accumulators
+    (8, 28, 28, 256, 128, torch.bfloat16, False, None),  # 6272 pixels: many tiles of up to 28 blocks
+    (2, 6, 10, 128, 72, torch.bfloat16, False, 200),     # X pixels 200 channels apart (a channel slice)
+]
+
+
+@pytest.mark.parametrize("case", POINTWISE)
+def test_gpu_pointwise_kernel(case):
+    N, H, W, C, O, odt, has_bias, xstride = case
+    seed = 7600 + POINTWISE.index(case)
+    base = wl.random_tensor((N, H, W, xstride or C), seed).to(torch.bfloat16)
+    X = base[..., :C]
+    F = (wl.random_tensor((1, 1, C, O), seed + 1) * (1.0 / C ** 0.5)).to(torch.bfloat16)
+    b = wl.random_tensor((O,), seed + 2) if has_bias else None
+    ref = oracle.conv2d_nhwc(X, F, bias=b)
+    y = cf.conv2d_nhwc(base.to(DEV)[..., :C], F.to(DEV), bias=None if b is None else b.to(DEV), out_dtype=odt)
+    torch.cuda.synchronize()
+    assert y.dtype == odt
+    if odt == torch.float32:
+        from parity import max_rel_err
+        assert max_rel_err(y, ref) <= 1e-5
+    else:
+        assert rms_rel_err(y, ref) <= BF16_RMS_REL
+        assert bf16_rounding_ok(y, ref, abs_sum_dense(oracle, X, F, bias=b), C)
+
+
+def test_gpu_pointwise_kernel_integer_bitwise():
+    g = torch.Generator().manual_seed(7700)
+    X = torch.randint(-1, 2, (4, 12, 13, 256), generator=g).to(torch.bfloat16)
+    F = torch.randint(-1, 2, (1, 1, 256, 256), generator=g).to(torch.bfloat16)
+    ref = oracle.conv2d_nhwc(X, F)
+    assert np.max(np.abs(ref)) <= 256
+    y = cf.conv2d_nhwc(X.to(DEV), F.to(DEV))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(y.float().cpu().numpy(), ref.astype(np.float32))
