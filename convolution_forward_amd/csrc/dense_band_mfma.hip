@@ -17,15 +17,18 @@
 // filter slice (K*K*Cin x 64) and R + K - 1 input rows before it is done.
 // Time spent waiting for the filter is time in which memory sits idle
 // unless the input rows are already on their way. So:
-//  * every input row of the band is requested in the first instructions,
+//  * every input row of the band is requested within the first two steps,
 //    with buffer loads that write straight into LDS (no registers held, no
-//    commit instructions); rows arrive in order and each step waits only
-//    for the row it is about to read;
+//    commit instructions); each step waits only for the row it is about to
+//    read;
 //  * the filter slice is requested one filter row (K taps) at a time: row 0
 //    and input rows 0-1 first (a barrier then makes every wave put these in
 //    the memory pipeline before any wave asks for more), then input row 2
-//    and the other filter rows, and the rest of the input at the start of
-//    step 0. The first step needs only filter row 0 and input rows 0-1, so
+//    and the other filter rows, input rows 3-5 at the start of step 0 and
+//    the last rows at the start of step 1, so that the memory system serves
+//    the rows needed first ahead of the later ones (all at once, they land
+//    together at the end). The first step needs only filter row 0 and input
+//    rows 0-1, so
 //    the matrix cores start after about a third of the filter has arrived
 //    instead of all of it. Filter row i is staged in LDS at step i - 1 and
 //    read into registers (gfx950 transpose read) at step i; two staging
@@ -40,14 +43,21 @@
 //    input row: K output rows accumulate at once, 2K independent chains per
 //    wave. The next row's fragments are read during the current row's
 //    MFMAs.
-//  * A finished output row is converted to bf16 (round to nearest even),
-//    regrouped through a small LDS patch private to the wave, and stored as
-//    16 bytes per lane: the four lanes of a pixel write one 64-byte run
-//    (half a cache line; the other half is the other wave's). Stores carry
+//  * For bf16 outputs the tile's output channels are staged in LDS in an
+//    order that gives each lane 8 consecutive channels of one pixel across
+//    its two 16-row MFMA blocks: MFMA row 4g + k of block nb is channel
+//    8g + 4nb + k of the wave's 32. A finished output row is converted to
+//    bf16 (round to nearest even) and stored straight from the accumulators
+//    as 16 bytes per lane, with no trip through LDS: the four lanes of a
+//    pixel write one 64-byte run (half a cache line; the other half is the
+//    other wave's). fp32 outputs keep the plain order (row m of block nb is
+//    channel 16nb + m), so that each store instruction writes 64-byte runs
+//    (4 channels per lane); with the bf16 order each would leave gaps and
+//    write partial lines, measured 1.6x slower. Stores carry
 //    the sc1 cache policy, measured on gfx950 to drain 64-byte runs about
 //    20% faster than the default; 32-byte runs (8 bytes per lane) take
 //    1.6x as long as whole lines.
-//  * Only the first KH steps end with a barrier (filter rows staged, input
+//  * Only the first few steps end with a barrier (filter rows staged, input
 //    rows published); the last of them waits for every input row, after
 //    which the waves run to the end without synchronising.
 //
@@ -86,10 +96,10 @@ typedef short i16x8 __attribute__((ext_vector_type(8)));
 constexpr int BT = 512;                  // threads per workgroup
 constexpr int TILE_O = 64;               // output channels per tile
 constexpr int NBW = 2;                   // 16-channel column blocks per wave
+static_assert(NBW == 2, "a lane's two blocks hold the 8 channels of one 16-byte store");
 constexpr int ROW_UNITS = 512;           // 16-byte units per staged input row
 constexpr int ROW_BYTES = ROW_UNITS * 16;
 constexpr int FPITCH = TILE_O + 8;       // LDS pitch of a staged filter row of 64 outputs (elements)
-constexpr int OP_PITCH = 80;             // LDS pitch of one pixel of a wave's output patch (bytes)
 constexpr int LDS_MAX = 160 * 1024;
 constexpr uint32_t OOB = 0x80000000u;    // buffer offset past every range: access dropped
 constexpr int BUF_WORD3 = 0x00020000;    // raw buffer descriptor word 3 (gfx9 family)
@@ -142,7 +152,8 @@ __device__ __forceinline__ void static_for(Fn &&fn)
     }
 }
 
-template <int KH, int KW, int CS, int NR, int ORDER = 0, int LS = KH - 1, bool OUT_BF16 = true>
+template <int KH, int KW, int CS, int NR, int ORDER = 0, int LS = KH - 1, bool OUT_BF16 = true, int LR = NR,
+          int LT = 0>
 struct BandShape {
     static constexpr int CINP = 32 * CS;
     static constexpr int CG = CINP / 8;                     // 16-byte units per pixel
@@ -156,7 +167,16 @@ struct BandShape {
     static constexpr int OSTORE = OUT_BF16 ? 1 : NBW;       // store instructions per output row and wave
     static constexpr int LAST_SYNC = LS;                    // last step that ends with a barrier
     static_assert(LS >= KH - 1 && LS + 2 < NR, "filter rows are staged at barriers; rows past LS + 1 exist");
-    static constexpr size_t LDS = (size_t)2 * FROW * 2 + (size_t)NR * ROW_BYTES + (BT / 64) * 16 * OP_PITCH;
+    // Late rows LR..NR-1 go out at the start of step LT (order 4 only): each
+    // must be requested before the step that waits for it.
+    static_assert(LR == NR || (ORDER == 4 && LR >= EARLY && LT >= 1 && LT <= LR - 2 && LT <= LS),
+                  "a late row is waited for before it is requested");
+    // Step at whose start input row q is requested (-1: the prologue).
+    static constexpr int issue_step(int q)
+    {
+        return q < EARLY || ORDER == 0 || ORDER == 2 ? -1 : q < LR ? 0 : LT;
+    }
+    static constexpr size_t LDS = (size_t)2 * FROW * 2 + (size_t)NR * ROW_BYTES;
 
     // Output rows stored by the end of step r: row t completes (and is
     // stored) at step t + KH - 1.
@@ -174,20 +194,23 @@ struct BandShape {
     // filter rows 1..KH-1 also issued at the start of step 0 (before the
     // other input rows). Order 4: as order 1, with a barrier after input
     // row 1, so that every wave's first loads reach the memory pipeline
-    // before any wave's later ones.
+    // before any wave's later ones; with LR < NR, rows LR..NR-1 only at the
+    // start of step LT.
     static constexpr int after_row(int q, int r)
     {
         if (ORDER == 3 && r < 0)
             return EARLY - 1 - q;                           // only the early rows are out
-        int n = NR - 1 - q;                                 // later rows
-        if ((ORDER == 1 || ORDER == 3 || ORDER == 4) && r < 0)
-            n -= NR - EARLY;                                // not issued yet
+        int n = 0;
+        for (int k = q + 1; k < NR; ++k)                    // later rows requested by then
+            n += issue_step(k) <= r ? 1 : 0;
         if (q < EARLY)
             n += FITEMS * (KH - 1);                         // filter rows 1..KH-1
         if (ORDER == 2 && q < 2)
             n += FITEMS + NBW;                              // filter row 0 and bias
-        if (r >= 0)
-            n += OSTORE * stores_by(r);
+        if (r >= 0) {                                       // stores of the steps from q's request on
+            const int s0 = issue_step(q);
+            n += OSTORE * (stores_by(r) - (s0 <= 0 ? 0 : stores_by(s0 - 1)));
+        }
         return n;
     }
 };
@@ -249,11 +272,11 @@ __device__ __forceinline__ void tr_reads(uint32_t base, i16x4 (&p)[B::TRN])
 
 #undef CF_TR
 
-template <int KH, int KW, int CS, int NR, int SAUX, int ORDER, int LS, bool OUT_BF16>
+template <int KH, int KW, int CS, int NR, int SAUX, int ORDER, int LS, bool OUT_BF16, int LR, int LT>
 __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void dense_band_mfma(BandArgs a)
 {
-    using B = BandShape<KH, KW, CS, NR, ORDER, LS, OUT_BF16>;
+    using B = BandShape<KH, KW, CS, NR, ORDER, LS, OUT_BF16, LR, LT>;
     constexpr int ESZ = OUT_BF16 ? 2 : 4;
     constexpr int CINP = B::CINP;
     constexpr int CG = B::CG;
@@ -325,13 +348,25 @@ void dense_band_mfma(BandArgs a)
                 fr, (fok && j < KW) ? fgoff + (uint32_t)(i * KW + j) * ftap : OOB, 0, 0);
         }
     };
+    // bf16 outputs: channels 8g + 4nb + k of a 32-channel half (g = fog % 4)
+    // sit in staged column 16nb + 4g + k of that half, which the MFMA blocks
+    // read as row 4g + k of block nb: the item's two 4-channel halves go to
+    // columns 4g and 16 + 4g. fp32 outputs: columns in channel order.
+    const int fcol = OUT_BF16 ? (fog >> 2) * 32 + (fog & 3) * 4 : fog * 8;
     auto commit_frow = [&](const int i) __attribute__((always_inline)) {
         uint16_t *ft = farea + (i & 1) * B::FROW;
 #pragma unroll
         for (int t = 0; t < B::FITEMS; ++t) {
             const int j = fj0 + t * JSTEP;
-            if (j < KW)
-                *reinterpret_cast<u32x4 *>(ft + (j * CINP + fc) * FPITCH + fog * 8) = fv[i][t];
+            if (j < KW) {
+                uint16_t *at = ft + (j * CINP + fc) * FPITCH + fcol;
+                if constexpr (OUT_BF16) {
+                    *reinterpret_cast<u32x2 *>(at) = u32x2{fv[i][t][0], fv[i][t][1]};
+                    *reinterpret_cast<u32x2 *>(at + 16) = u32x2{fv[i][t][2], fv[i][t][3]};
+                } else {
+                    *reinterpret_cast<u32x4 *>(at) = fv[i][t];
+                }
+            }
         }
     };
     // A fragments of filter row i (k-steps i*KSR ..). Within each 16-lane
@@ -377,8 +412,9 @@ void dense_band_mfma(BandArgs a)
             xr, (__attribute__((address_space(3))) void *)(xrows + r * ROW_BYTES + wave * 1024), 16, off, 0, 0, 0);
     };
 
-    // Bias of the 4 output channels of each column block a lane's results
-    // belong to (zeros without bias).
+    // Bias of the 4 output channels of each MFMA block a lane's results
+    // belong to (zeros without bias): 32*half + 8*(lane/16) + 4*nb + {0..3}
+    // for bf16 outputs, 32*half + 16*nb + 4*(lane/16) + {0..3} for fp32.
     u32x4 bq[NBW];
     auto issue_bias = [&]() __attribute__((always_inline)) {
         const __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc(
@@ -386,7 +422,8 @@ void dense_band_mfma(BandArgs a)
 #pragma unroll
         for (int nb = 0; nb < NBW; ++nb)
             bq[nb] = __builtin_amdgcn_raw_buffer_load_b128(
-                br, (uint32_t)((o0 + half * 32 + nb * 16 + (lane >> 4) * 4) * 4), 0, 0);
+                br, (uint32_t)((o0 + half * 32 + (OUT_BF16 ? (lane >> 4) * 8 + nb * 4 : nb * 16 + (lane >> 4) * 4)) * 4),
+                0, 0);
     };
 
     // Issue order (the vmcnt bookkeeping in BandShape::after_row depends on
@@ -447,11 +484,8 @@ void dense_band_mfma(BandArgs a)
     bf16x8 xn[KSR];
     read_x(0, xn);
 
-    // The wave's output patch (16 pixels x 64 bytes, pitch 80 bytes: the 16
-    // lanes reading one 16-byte column hit distinct banks) and the store
-    // target of this lane after the regrouping: pixel pg*16 + lane % 16,
-    // channels 32*half + 8*(lane/16) .. +7.
-    uint8_t *opatch = xrows + NR * ROW_BYTES + wave * 16 * OP_PITCH;
+    // Store target of this lane: pixel pg*16 + lane % 16, channels
+    // 32*half + 8*(lane/16) .. +7 (block nb holds the 4 from 4*nb).
     const int xs_px = pg * 16 + (lane & 15);
     const int xs_ch = o0 + half * 32 + (lane >> 4) * 8;
     const bool xs_ok = xs_px < a.Wo && xs_ch < a.Cout;
@@ -463,6 +497,44 @@ void dense_band_mfma(BandArgs a)
 #pragma unroll
         for (int nb = 0; nb < NBW; ++nb)
             acc[s][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // Output row t is complete: bias, conversion, store; its accumulators
+    // are cleared for the row that reuses the slot.
+    auto store_row = [&](auto TT) __attribute__((always_inline)) {
+        constexpr int t = decltype(TT)::value;
+        const int yo = y0 + t;
+        if constexpr (!OUT_BF16) {
+            // Channels 32*half + 16*nb + 4*(lane/16) + {0..3} of pixel x, 16
+            // fp32 bytes: the four lanes of a pixel write one 64-byte run.
+#pragma unroll
+            for (int nb = 0; nb < NBW; ++nb) {
+                const f32x4 v = acc[t % KH][nb];
+                const u32x4 w = {__float_as_uint(v[0] + __uint_as_float(bq[nb][0])),
+                                 __float_as_uint(v[1] + __uint_as_float(bq[nb][1])),
+                                 __float_as_uint(v[2] + __uint_as_float(bq[nb][2])),
+                                 __float_as_uint(v[3] + __uint_as_float(bq[nb][3]))};
+                const int ch = o0 + half * 32 + nb * 16 + (lane >> 4) * 4;
+                const bool okc = x < a.Wo && ch < a.Cout && yo < y1;
+                const uint32_t off =
+                    okc ? (uint32_t)(((int64_t)yo * a.ys1 + (int64_t)x * a.ys2 + ch) * 4) : OOB;
+                __builtin_amdgcn_raw_buffer_store_b128(w, yr, off, 0, SAUX);
+                acc[t % KH][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+        } else {
+            // 8 bf16 channels, one 16-byte store.
+            const bool ok = xs_ok && yo < y1;
+            u32x4 w;
+#pragma unroll
+            for (int nb = 0; nb < NBW; ++nb) {
+                const f32x4 v = acc[t % KH][nb];
+                w[2 * nb] = pack_bf16x2(v[0] + __uint_as_float(bq[nb][0]), v[1] + __uint_as_float(bq[nb][1]));
+                w[2 * nb + 1] = pack_bf16x2(v[2] + __uint_as_float(bq[nb][2]), v[3] + __uint_as_float(bq[nb][3]));
+                acc[t % KH][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+            const uint32_t off = ok ? (uint32_t)(((int64_t)yo * a.ys1 + xs_off) * 2) : OOB;
+            __builtin_amdgcn_raw_buffer_store_b128(w, yr, off, 0, SAUX);
+        }
+    };
 
     // Step r: input row r feeds output rows t = r - i for filter rows i;
     // output row t accumulates in slot t % KH (taps in ascending i, then j,
@@ -481,7 +553,12 @@ void dense_band_mfma(BandArgs a)
             __builtin_amdgcn_sched_barrier(0);
             if constexpr (ORDER == 3)
                 static_for<1, KH>([&](auto I) { issue_frow(decltype(I)::value); });
-            static_for<B::EARLY, NR>([&](auto R) { dma_row(decltype(R)::value); });
+            static_for<B::EARLY, LR>([&](auto R) { dma_row(decltype(R)::value); });
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if constexpr (LR < NR && r == LT) {
+            __builtin_amdgcn_sched_barrier(0);
+            static_for<LR, NR>([&](auto R) { dma_row(decltype(R)::value); });
             __builtin_amdgcn_sched_barrier(0);
         }
         bf16x8 xb[KSR];
@@ -490,9 +567,9 @@ void dense_band_mfma(BandArgs a)
             xb[jc] = xn[jc];
         if constexpr (r + 1 < NR)
             read_x(r + 1, xn);
-        // Filter rows already in registers first (all of them from step KH
-        // on; rows 0..r-1 at step r < KH, row 0 at step 0), then, at steps
-        // 1..KH-1, filter row r once its fragments are read.
+        // Filter rows already in registers first (all of them from step
+        // KH on; rows 0..r-1 at step r < KH, row 0 at step 0), then, at
+        // steps 1..KH-1, filter row r once its fragments are read.
         constexpr int IA = r < 1 ? 1 : r < KH ? r : KH;
 #pragma unroll
         for (int jc = 0; jc < KSR; ++jc)
@@ -518,47 +595,8 @@ void dense_band_mfma(BandArgs a)
         }
         if constexpr (r + 1 < KH)
             commit_frow(r + 1);
-        if constexpr (r >= KH - 1 && r - (KH - 1) < RMAX && !OUT_BF16) {
-            // Output row t is complete: the lane holds channels
-            // 32*half + 16*nb + 4*(lane/16) + {0..3} of pixel x, 16 bytes in
-            // fp32; the four lanes of a pixel write one 64-byte run.
-            constexpr int t = r - (KH - 1);
-            const int yo = y0 + t;
-#pragma unroll
-            for (int nb = 0; nb < NBW; ++nb) {
-                const f32x4 v = acc[t % KH][nb];
-                const u32x4 w = {__float_as_uint(v[0] + __uint_as_float(bq[nb][0])),
-                                 __float_as_uint(v[1] + __uint_as_float(bq[nb][1])),
-                                 __float_as_uint(v[2] + __uint_as_float(bq[nb][2])),
-                                 __float_as_uint(v[3] + __uint_as_float(bq[nb][3]))};
-                const int ch = o0 + half * 32 + nb * 16 + (lane >> 4) * 4;
-                const bool ok = x < a.Wo && ch < a.Cout && yo < y1;
-                const uint32_t off = ok ? (uint32_t)(((int64_t)yo * a.ys1 + (int64_t)x * a.ys2 + ch) * 4) : OOB;
-                __builtin_amdgcn_raw_buffer_store_b128(w, yr, off, 0, SAUX);
-                acc[t % KH][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-            }
-        }
-        if constexpr (r >= KH - 1 && r - (KH - 1) < RMAX && OUT_BF16) {
-            // Output row t is complete: the lane holds channels
-            // 32*half + 16*nb + 4*(lane/16) + {0..3} of pixel x. The wave
-            // regroups its 16 pixels x 32 channels through its own LDS
-            // patch so that each lane holds 8 consecutive channels (16
-            // bytes) and the four lanes of a pixel write one 64-byte run.
-            constexpr int t = r - (KH - 1);
-#pragma unroll
-            for (int nb = 0; nb < NBW; ++nb) {
-                const f32x4 v = acc[t % KH][nb];
-                *reinterpret_cast<u32x2 *>(opatch + (lane & 15) * OP_PITCH + nb * 32 + (lane >> 4) * 8) =
-                    u32x2{pack_bf16x2(v[0] + __uint_as_float(bq[nb][0]), v[1] + __uint_as_float(bq[nb][1])),
-                          pack_bf16x2(v[2] + __uint_as_float(bq[nb][2]), v[3] + __uint_as_float(bq[nb][3]))};
-                acc[t % KH][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-            }
-            const u32x4 w = *reinterpret_cast<const u32x4 *>(opatch + (lane & 15) * OP_PITCH + (lane >> 4) * 16);
-            const int yo = y0 + t;
-            const bool ok = xs_ok && yo < y1;
-            const uint32_t off = ok ? (uint32_t)(((int64_t)yo * a.ys1 + xs_off) * 2) : OOB;
-            __builtin_amdgcn_raw_buffer_store_b128(w, yr, off, 0, SAUX);
-        }
+        if constexpr (r >= KH - 1 && r - (KH - 1) < RMAX)
+            store_row(std::integral_constant<int, r - (KH - 1)>{});
         if constexpr (r < B::LAST_SYNC) {
             // Row r + 2 is read (as the next row's fragments) during step r + 1.
             wait_vmcnt<B::after_row(r + 2, r)>();
@@ -570,11 +608,13 @@ void dense_band_mfma(BandArgs a)
     });
 }
 
-template <int KH, int KW, int CS, int NR, bool OB, int SAUX = 16, int ORDER = 4, int LS = KH - 1>
+// Defaults measured on the 3x3 layers: rows 6..8 requested at step 1 (so
+// that rows 3..5 reach the memory system first), barriers through step 3.
+template <int KH, int KW, int CS, int NR, bool OB, int SAUX = 16, int ORDER = 4, int LS = 3, int LR = 6, int LT = 1>
 hipError_t launch_band(const BandArgs &a, dim3 grid, hipStream_t s)
 {
-    auto kern = dense_band_mfma<KH, KW, CS, NR, SAUX, ORDER, LS, OB>;
-    constexpr size_t lds = BandShape<KH, KW, CS, NR, ORDER, LS, OB>::LDS;
+    auto kern = dense_band_mfma<KH, KW, CS, NR, SAUX, ORDER, LS, OB, LR, LT>;
+    constexpr size_t lds = BandShape<KH, KW, CS, NR, ORDER, LS, OB, LR, LT>::LDS;
     static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (attr != hipSuccess)
