@@ -152,8 +152,7 @@ __device__ __forceinline__ void static_for(Fn &&fn)
     }
 }
 
-template <int KH, int KW, int CS, int NR, int ORDER = 0, int LS = KH - 1, bool OUT_BF16 = true, int LR = NR,
-          int LT = 0>
+template <int KH, int KW, int CS, int NR, int LS, bool OUT_BF16, int LR, int LT>
 struct BandShape {
     static constexpr int CINP = 32 * CS;
     static constexpr int CG = CINP / 8;                     // 16-byte units per pixel
@@ -167,15 +166,12 @@ struct BandShape {
     static constexpr int OSTORE = OUT_BF16 ? 1 : NBW;       // store instructions per output row and wave
     static constexpr int LAST_SYNC = LS;                    // last step that ends with a barrier
     static_assert(LS >= KH - 1 && LS + 2 < NR, "filter rows are staged at barriers; rows past LS + 1 exist");
-    // Late rows LR..NR-1 go out at the start of step LT (order 4 only): each
-    // must be requested before the step that waits for it.
-    static_assert(LR == NR || (ORDER == 4 && LR >= EARLY && LT >= 1 && LT <= LR - 2 && LT <= LS),
+    // Late rows LR..NR-1 go out at the start of step LT: each must be
+    // requested before the step that waits for it.
+    static_assert(LR == NR || (LR >= EARLY && LT >= 1 && LT <= LR - 2 && LT <= LS),
                   "a late row is waited for before it is requested");
     // Step at whose start input row q is requested (-1: the prologue).
-    static constexpr int issue_step(int q)
-    {
-        return q < EARLY || ORDER == 0 || ORDER == 2 ? -1 : q < LR ? 0 : LT;
-    }
+    static constexpr int issue_step(int q) { return q < EARLY ? -1 : q < LR ? 0 : LT; }
     static constexpr size_t LDS = (size_t)2 * FROW * 2 + (size_t)NR * ROW_BYTES;
 
     // Output rows stored by the end of step r: row t completes (and is
@@ -186,27 +182,19 @@ struct BandShape {
         return s < 0 ? 0 : s > RMAX ? RMAX : s;
     }
     // Memory instructions a wave has issued after input row q's load, by
-    // the end of step r (r >= 0), or in the prologue (r = -1). Issue order
-    // 0: bias, filter row 0, input rows 0..EARLY-1, filter rows 1..KH-1,
-    // the other input rows. Order 1: the same, but the other input rows
-    // only at the start of step 0. Order 2: input rows 0 and 1 first, then
-    // bias and filter row 0, then as order 0. Order 3: as order 1, with
-    // filter rows 1..KH-1 also issued at the start of step 0 (before the
-    // other input rows). Order 4: as order 1, with a barrier after input
-    // row 1, so that every wave's first loads reach the memory pipeline
-    // before any wave's later ones; with LR < NR, rows LR..NR-1 only at the
-    // start of step LT.
+    // the end of step r (r >= 0), or in the prologue (r = -1). Issue order:
+    // bias, filter row 0, input rows 0 and 1, a barrier (every wave's first
+    // loads reach the memory pipeline before any wave's later ones), input
+    // rows 2..EARLY-1, filter rows 1..KH-1; input rows EARLY..LR-1 at the
+    // start of step 0 and rows LR..NR-1 at the start of step LT; one output
+    // row's stores (OSTORE instructions) at each step from KH-1 on.
     static constexpr int after_row(int q, int r)
     {
-        if (ORDER == 3 && r < 0)
-            return EARLY - 1 - q;                           // only the early rows are out
         int n = 0;
         for (int k = q + 1; k < NR; ++k)                    // later rows requested by then
             n += issue_step(k) <= r ? 1 : 0;
         if (q < EARLY)
             n += FITEMS * (KH - 1);                         // filter rows 1..KH-1
-        if (ORDER == 2 && q < 2)
-            n += FITEMS + NBW;                              // filter row 0 and bias
         if (r >= 0) {                                       // stores of the steps from q's request on
             const int s0 = issue_step(q);
             n += OSTORE * (stores_by(r) - (s0 <= 0 ? 0 : stores_by(s0 - 1)));
@@ -272,11 +260,11 @@ __device__ __forceinline__ void tr_reads(uint32_t base, i16x4 (&p)[B::TRN])
 
 #undef CF_TR
 
-template <int KH, int KW, int CS, int NR, int SAUX, int ORDER, int LS, bool OUT_BF16, int LR, int LT>
+template <int KH, int KW, int CS, int NR, int SAUX, int LS, bool OUT_BF16, int LR, int LT>
 __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void dense_band_mfma(BandArgs a)
 {
-    using B = BandShape<KH, KW, CS, NR, ORDER, LS, OUT_BF16, LR, LT>;
+    using B = BandShape<KH, KW, CS, NR, LS, OUT_BF16, LR, LT>;
     constexpr int ESZ = OUT_BF16 ? 2 : 4;
     constexpr int CINP = B::CINP;
     constexpr int CG = B::CG;
@@ -428,33 +416,15 @@ void dense_band_mfma(BandArgs a)
 
     // Issue order (the vmcnt bookkeeping in BandShape::after_row depends on
     // it; the scheduling fences keep the compiler from reordering).
-    if constexpr (ORDER == 2) {
-        static_for<0, 2>([&](auto R) { dma_row(decltype(R)::value); });
-        __builtin_amdgcn_sched_barrier(0);
-        issue_bias();
-        issue_frow(0);
-        __builtin_amdgcn_sched_barrier(0);
-        static_for<2, B::EARLY>([&](auto R) { dma_row(decltype(R)::value); });
-    } else if constexpr (ORDER == 4) {
-        issue_bias();
-        issue_frow(0);
-        __builtin_amdgcn_sched_barrier(0);
-        static_for<0, 2>([&](auto R) { dma_row(decltype(R)::value); });
-        __builtin_amdgcn_sched_barrier(0);
-        asm volatile("s_barrier" ::: "memory");
-        static_for<2, B::EARLY>([&](auto R) { dma_row(decltype(R)::value); });
-    } else {
-        issue_bias();
-        issue_frow(0);
-        __builtin_amdgcn_sched_barrier(0);
-        static_for<0, B::EARLY>([&](auto R) { dma_row(decltype(R)::value); });
-    }
+    issue_bias();
+    issue_frow(0);
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (ORDER != 3)
-        static_for<1, KH>([&](auto I) { issue_frow(decltype(I)::value); });
+    static_for<0, 2>([&](auto R) { dma_row(decltype(R)::value); });
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (ORDER == 0 || ORDER == 2)
-        static_for<B::EARLY, NR>([&](auto R) { dma_row(decltype(R)::value); });
+    asm volatile("s_barrier" ::: "memory");
+    static_for<2, B::EARLY>([&](auto R) { dma_row(decltype(R)::value); });
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<1, KH>([&](auto I) { issue_frow(decltype(I)::value); });
     __builtin_amdgcn_sched_barrier(0);
 
     // Filter row 0 into LDS, input rows 0 and 1 landed, then the first
@@ -549,10 +519,8 @@ void dense_band_mfma(BandArgs a)
     // steps need no barrier at all and the waves run freely to the end.
     static_for<0, NR>([&](auto RR) {
         constexpr int r = decltype(RR)::value;
-        if constexpr ((ORDER == 1 || ORDER == 3 || ORDER == 4) && r == 0) {
+        if constexpr (r == 0) {
             __builtin_amdgcn_sched_barrier(0);
-            if constexpr (ORDER == 3)
-                static_for<1, KH>([&](auto I) { issue_frow(decltype(I)::value); });
             static_for<B::EARLY, LR>([&](auto R) { dma_row(decltype(R)::value); });
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -610,11 +578,11 @@ void dense_band_mfma(BandArgs a)
 
 // Defaults measured on the 3x3 layers: rows 6..8 requested at step 1 (so
 // that rows 3..5 reach the memory system first), barriers through step 3.
-template <int KH, int KW, int CS, int NR, bool OB, int SAUX = 16, int ORDER = 4, int LS = 3, int LR = 6, int LT = 1>
+template <int KH, int KW, int CS, int NR, bool OB, int SAUX = 16, int LS = 3, int LR = 6, int LT = 1>
 hipError_t launch_band(const BandArgs &a, dim3 grid, hipStream_t s)
 {
-    auto kern = dense_band_mfma<KH, KW, CS, NR, SAUX, ORDER, LS, OB, LR, LT>;
-    constexpr size_t lds = BandShape<KH, KW, CS, NR, ORDER, LS, OB, LR, LT>::LDS;
+    auto kern = dense_band_mfma<KH, KW, CS, NR, SAUX, LS, OB, LR, LT>;
+    constexpr size_t lds = BandShape<KH, KW, CS, NR, LS, OB, LR, LT>::LDS;
     static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (attr != hipSuccess)
