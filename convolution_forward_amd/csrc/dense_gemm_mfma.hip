@@ -29,8 +29,11 @@
 //    straight from X for each step, one step ahead of use. Taps in the
 //    padding and pixels past the end use out-of-range buffer offsets, which
 //    load zeros without touching memory.
-//  * Results leave straight from the accumulators: each lane stores the 4
-//    consecutive output channels it holds for one pixel.
+//  * bf16 results are regrouped through the (by then idle) filter buffer:
+//    each wave parks its 64 pixels x 64 channels there, then eight lanes
+//    store each pixel's 128-byte row whole (stores of 8 bytes in 32-byte
+//    runs drain several times slower). fp32 results leave straight from the
+//    accumulators, 16 bytes per lane in 64-byte runs.
 #include <type_traits>
 
 #include "common.h"
@@ -55,6 +58,8 @@ constexpr int KC = 4;                   // 32-channel steps per filter chunk
 constexpr int FP = GN + 8;              // LDS row pitch of a filter chunk (elements)
 constexpr int CHUNK_ELEMS = KC * 32 * FP;
 constexpr int FITEMS = KC * 32 * (GN / 8) / GT;   // 16-byte filter loads per thread per chunk
+constexpr int OPITCH = GN * 2 + 16;     // LDS pitch of one pixel of a wave's bf16 output patch (bytes)
+static_assert(GT / 64 * 64 * OPITCH <= 2 * CHUNK_ELEMS * 2, "output patches fit in the filter buffer");
 constexpr uint32_t OOB = 0x80000000u;
 constexpr int BUF_WORD3 = 0x00020000;
 
@@ -243,29 +248,57 @@ __global__ __launch_bounds__(GT) void dense_gemm_mfma(GemmArgs a)
     // each block.
     const __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc(
         a.bias ? (void *)(a.bias + oc0) : (void *)a.F, 0, a.bias ? (int)a.b_records : 0, BUF_WORD3);
+    u32x4 bq[NB];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-        const int ch = o0 + nb * 16 + g * 4;
-        const u32x4 bq = __builtin_amdgcn_raw_buffer_load_b128(br, (uint32_t)(ch * 4), 0, 0);
+    for (int nb = 0; nb < NB; ++nb)
+        bq[nb] = __builtin_amdgcn_raw_buffer_load_b128(br, (uint32_t)((o0 + nb * 16 + g * 4) * 4), 0, 0);
+    if constexpr (OUT_BF16) {
+        // Every wave is done with the filter buffer before any overwrites it.
+        __syncthreads();
+        uint8_t *patch = reinterpret_cast<uint8_t *>(&fbuf[0][0]) + wave * 64 * OPITCH;
 #pragma unroll
-        for (int b = 0; b < BLK; ++b) {
-            if (!mok[b] || ch >= a.Cout)
-                continue;
-            const f32x4 v = acc[b][nb];
-            const float v0 = v[0] + __uint_as_float(bq[0]);
-            const float v1 = v[1] + __uint_as_float(bq[1]);
-            const float v2 = v[2] + __uint_as_float(bq[2]);
-            const float v3 = v[3] + __uint_as_float(bq[3]);
-            char *yp = static_cast<char *>(a.Y) +
-                       ((int64_t)nb0[b] * a.ys0 + (int64_t)yo[b] * a.ys1 + (int64_t)xo[b] * a.ys2 + oc0 + ch) * ESZ;
-            if constexpr (OUT_BF16) {
-                const uint32_t lo = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v0) |
-                                    ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v1) << 16);
-                const uint32_t hi = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v2) |
-                                    ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v3) << 16);
-                *reinterpret_cast<u32x2 *>(yp) = u32x2{lo, hi};
-            } else {
-                *reinterpret_cast<f32x4 *>(yp) = f32x4{v0, v1, v2, v3};
+        for (int b = 0; b < BLK; ++b)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                const f32x4 v = acc[b][nb];
+                const uint32_t lo = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)(v[0] + __uint_as_float(bq[nb][0]))) |
+                                    ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)(v[1] + __uint_as_float(bq[nb][1]))) << 16);
+                const uint32_t hi = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)(v[2] + __uint_as_float(bq[nb][2]))) |
+                                    ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)(v[3] + __uint_as_float(bq[nb][3]))) << 16);
+                *reinterpret_cast<u32x2 *>(patch + (b * 16 + r) * OPITCH + (nb * 16 + g * 4) * 2) = u32x2{lo, hi};
+            }
+        // The patch is this wave's own: its LDS writes complete before its
+        // reads (in order), no barrier. Store i: lane L takes pixel
+        // 8i + L/8 of the wave's 64, channels 8*(L%8)..+7.
+        const int ch = o0 + (lane & 7) * 8;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int pp = i * 8 + (lane >> 3);
+            const u32x4 w = *reinterpret_cast<const u32x4 *>(patch + pp * OPITCH + (lane & 7) * 16);
+            const int m = mt * GM + wave * 64 + pp;
+            if (m < a.m_total && ch < a.Cout) {
+                const uint32_t ny = fdiv_g((uint32_t)m, a.div_wo);
+                const int x = (int)((uint32_t)m - ny * (uint32_t)a.Wo);
+                const uint32_t n = fdiv_g(ny, a.div_ho);
+                const int y = (int)(ny - n * (uint32_t)a.Ho);
+                char *yp = static_cast<char *>(a.Y) +
+                           ((int64_t)n * a.ys0 + (int64_t)y * a.ys1 + (int64_t)x * a.ys2 + oc0 + ch) * 2;
+                *reinterpret_cast<u32x4 *>(yp) = w;
+            }
+        }
+    } else {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const int ch = o0 + nb * 16 + g * 4;
+#pragma unroll
+            for (int b = 0; b < BLK; ++b) {
+                if (!mok[b] || ch >= a.Cout)
+                    continue;
+                const f32x4 v = acc[b][nb];
+                char *yp = static_cast<char *>(a.Y) +
+                           ((int64_t)nb0[b] * a.ys0 + (int64_t)yo[b] * a.ys1 + (int64_t)xo[b] * a.ys2 + oc0 + ch) * ESZ;
+                *reinterpret_cast<f32x4 *>(yp) = f32x4{v[0] + __uint_as_float(bq[nb][0]), v[1] + __uint_as_float(bq[nb][1]),
+                                                       v[2] + __uint_as_float(bq[nb][2]), v[3] + __uint_as_float(bq[nb][3])};
             }
         }
     }
@@ -284,6 +317,9 @@ bool dense_gemm_bf16_supports(const DenseProblem &p)
         return false;
     const int yesz = p.ydt == CONV_BF16 ? 2 : 4;
     if ((uintptr_t)p.Y % (4 * yesz) != 0 || p.ys[0] % 4 != 0 || p.ys[1] % 4 != 0 || p.ys[2] % 4 != 0)
+        return false;
+    // bf16 rows leave in 16-byte pieces of 8 channels.
+    if (p.ydt == CONV_BF16 && ((uintptr_t)p.Y % 16 != 0 || p.ys[0] % 8 != 0 || p.ys[1] % 8 != 0 || p.ys[2] % 8 != 0))
         return false;
     if ((uintptr_t)p.F % 16 != 0)
         return false;
