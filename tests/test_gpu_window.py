@@ -158,3 +158,30 @@ def test_gpu_depthwise_window_bitwise(case, mode):
         outs.append(Y)
     if name == "asym_tiled_3x3" or name.startswith("row_") or name == "causal_dw_conv1d":
         assert cf.depthwise_variant_for((N, C, H, W), (C * m, KH, KW), stride, padding, dilation) == cf.VARIANT_TILED
+
+
+@pytest.mark.parametrize("total,offset", [(136, 64), (76, 2)], ids=["aligned_slice", "unaligned_slice"])
+def test_gpu_gemm_bf16_into_channel_slice(total, offset):
+    """A window only the streamed GEMM kernel takes, written as bf16 into a
+    channel slice of a wider buffer. With a 16-byte aligned slice and pixel
+    stride the kernel's whole-row stores run; otherwise another variant takes
+    the call. Either way the slice gets the contract's values and nothing
+    outside it is written."""
+    X = wl.random_tensor((2, 14, 15, 128), 9300).to(torch.bfloat16)
+    F = (wl.random_tensor((3, 3, 128, 72), 9301) * (1.0 / (9 * 128) ** 0.5)).to(torch.bfloat16)
+    b = wl.random_tensor((72,), 9302)
+    ref = dense_ref(X, F, b, 1, 1, 1, 1)
+    buf = torch.full((2, 14, 15, total), float("nan"), dtype=torch.bfloat16, device=DEV)
+    out = buf[..., offset:offset + 72]
+    y = cf.conv2d_nhwc(X.to(DEV), F.to(DEV), bias=b.to(DEV), padding=1, out=out)
+    y32 = cf.conv2d_nhwc(X.to(DEV), F.to(DEV), bias=b.to(DEV), padding=1, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert y.data_ptr() == out.data_ptr()
+    assert rms_rel_err(out, ref) <= BF16_RMS_REL
+    absref = dense_ref(X.float().abs(), F.float().abs(), b.abs(), 1, 1, 1, 1)
+    assert bf16_rounding_ok(out, ref, absref, 9 * 128)
+    if offset % 8 == 0:
+        # same kernel and accumulation as the fp32 call: its rounding, bit for bit
+        assert torch.equal(out.cpu().view(torch.int16), y32.cpu().to(torch.bfloat16).view(torch.int16))
+    outside = torch.cat([buf[..., :offset], buf[..., offset + 72:]], dim=-1)
+    assert torch.isnan(outside.float()).all()
