@@ -283,11 +283,11 @@ void dense_rows_mfma(RowArgs a)
     constexpr int OTILE_BYTES = 64 * BPW * OPITCH;
     constexpr int OCH = COUT_TILE * ESZ / 16;                        // 16-byte chunks per pixel
     constexpr int OSTORE = (64 * BPW * OCH + THREADS - 1) / THREADS;  // store instructions per row
-    // Store cache policy: sc1 drains whole-line stores faster on gfx950
-    // (measured: fp32 outputs and windowed layers 3-6% faster); the 1x1
-    // bf16 layer, whose stores interleave with a long X stream, keeps the
-    // default.
-    constexpr int SAUX = (KH == 1 && OUT_BF16) ? 0 : 16;
+    // Store cache policy: sc1 | nt drains whole-line stores faster on
+    // gfx950 (measured: fp32 outputs and windowed layers 3-6% faster with
+    // sc1, nt adds a little); the 1x1 bf16 layer, whose stores interleave
+    // with a long X stream, keeps the default.
+    constexpr int SAUX = (KH == 1 && OUT_BF16) ? 0 : 18;
 
     // LDS: [filter staging] [two input-row buffers] [output tiles], or, when
     // that does not fit, [filter staging, later the row buffers] [output
