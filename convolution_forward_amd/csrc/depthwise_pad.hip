@@ -205,7 +205,9 @@ __global__ __launch_bounds__(THREADS) void dw_pad_kernel(PadArgs a)
                 r = r + bv;
             if (EXACT && __builtin_isnan(r))
                 r = __uint_as_float(0x7FC00000u);
-            yp[(int64_t)oy * a.Wo] = r;
+            // Streaming (nt) stores: the 112-wide planes 3-5% faster; the
+            // contiguous-range kernel's short rows are slower with them.
+            __builtin_nontemporal_store(r, &yp[(int64_t)oy * a.Wo]);
         }
     }
 }
