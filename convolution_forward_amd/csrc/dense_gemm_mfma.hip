@@ -283,7 +283,7 @@ __global__ __launch_bounds__(GT) void dense_gemm_mfma(GemmArgs a)
                 const int y = (int)(ny - n * (uint32_t)a.Ho);
                 char *yp = static_cast<char *>(a.Y) +
                            ((int64_t)n * a.ys0 + (int64_t)y * a.ys1 + (int64_t)x * a.ys2 + oc0 + ch) * 2;
-                *reinterpret_cast<u32x4 *>(yp) = w;
+                __builtin_nontemporal_store(w, reinterpret_cast<u32x4 *>(yp));   // nt: Conv1D stem -2.5 %
             }
         }
     } else {
