@@ -14,6 +14,7 @@ import numpy as np
 import pytest
 import torch
 
+import bench
 import convolution_forward_amd as cf
 import oracle
 import workloads as wl
@@ -185,3 +186,43 @@ def test_gpu_gemm_bf16_into_channel_slice(total, offset):
         assert torch.equal(out.cpu().view(torch.int16), y32.cpu().to(torch.bfloat16).view(torch.int16))
     outside = torch.cat([buf[..., :offset], buf[..., offset + 72:]], dim=-1)
     assert torch.isnan(outside.float()).all()
+
+
+def _sample_flat(shape, n, seed):
+    """Random flat output indices plus every output of the first and last
+    rows and columns of the first and last images (the padded borders)."""
+    N, Ho, Wo, O = shape
+    rng = np.random.default_rng(seed)
+    idx = set(rng.integers(0, N * Ho * Wo * O, size=n).tolist())
+    for nn in (0, N - 1):
+        for y in sorted({0, Ho - 1}):
+            for x in range(Wo):
+                idx.update(((nn * Ho + y) * Wo + x) * O + o for o in (0, O // 2, O - 1))
+        for y in range(Ho):
+            for x in sorted({0, Wo - 1}):
+                idx.update(((nn * Ho + y) * Wo + x) * O + o for o in (0, O // 2, O - 1))
+    return np.array(sorted(idx), dtype=np.int64)
+
+
+@pytest.mark.parametrize("layer", bench.WINDOW_LAYERS, ids=lambda l: l[0].split(" (")[0].replace(" ", "_"))
+def test_gpu_window_layer_full_size_sampled(layer):
+    """The window layers the benchmark times, at their full sizes, on the
+    tiled MFMA path: 20,000 sampled outputs plus the padded borders against
+    the oracle, bias included."""
+    name, (N, H, W, C), (KH, KW, O), stride, padding, groups, _ = layer
+    seed = 9400 + bench.WINDOW_LAYERS.index(layer)
+    X = wl.random_tensor((N, H, W, C), seed).to(torch.bfloat16)
+    F = (wl.random_tensor((KH, KW, C // groups, O), seed + 1) * (1.0 / (KH * KW * C / groups) ** 0.5)).to(torch.bfloat16)
+    b = wl.random_tensor((O,), seed + 2)
+    kw = dict(stride=stride, padding=padding, groups=groups)
+    Xd, Fd = X.to(DEV), F.to(DEV)
+    assert cf.dense_variant_for(Xd, Fd, **kw) == cf.VARIANT_TILED
+    Y = cf.conv2d_nhwc(Xd, Fd, bias=b.to(DEV), **kw)
+    torch.cuda.synchronize()
+    idx = _sample_flat(tuple(Y.shape), 20000, seed)
+    ref = oracle.conv2d_nhwc_at(X, F, idx, bias=b, **kw)
+    got = Y.reshape(-1)[torch.from_numpy(idx).to(DEV)]
+    assert rms_rel_err(got, ref) <= BF16_RMS_REL
+    absref = oracle.conv2d_nhwc_at(X.float().abs(), F.float().abs(), idx, bias=b.abs(), **kw)
+    assert bf16_rounding_ok(got, ref, absref, KH * KW * C // groups)
+    assert torch.isfinite(Y.float()).all()
