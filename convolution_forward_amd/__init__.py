@@ -45,7 +45,8 @@ VARIANT_TILED = 2
 EXPORTED = ("conv2d_nhwc_fwd", "conv2d_nhwc_fwd_variant", "conv2d_nhwc_fwd_window", "conv_depthwise_fwd",
             "conv_depthwise_fwd_variant", "conv_depthwise_fwd_window", "conv2d_nhwc_auto_variant",
             "conv2d_nhwc_window_auto_variant", "conv_depthwise_auto_variant", "conv_depthwise_window_auto_variant",
-            "conv_out_size", "conv_out_size_window", "conv_status_str", "conv_copy_bytes", "conv_im2col_nhwc")
+            "conv_out_size", "conv_out_size_window", "conv_status_str", "conv_copy_bytes", "conv_copy_bytes_wide",
+            "conv_im2col_nhwc")
 
 
 class ConvWindow(ctypes.Structure):
@@ -89,9 +90,9 @@ def load_library():
     lib.conv_depthwise_fwd_variant.restype = i
     lib.conv_depthwise_fwd_variant.argtypes = [p, p, p, p] + [i] * 13 + [i, i, p]
     lib.conv2d_nhwc_auto_variant.restype = i
-    lib.conv2d_nhwc_auto_variant.argtypes = [p, p] + [i] * 7 + [i, i]
+    lib.conv2d_nhwc_auto_variant.argtypes = [p, p, p, p, p, p] + [i] * 7 + [i, i]
     lib.conv_depthwise_auto_variant.restype = i
-    lib.conv_depthwise_auto_variant.argtypes = [i] * 13
+    lib.conv_depthwise_auto_variant.argtypes = [p, p, p, p] + [i] * 13 + [i]
     lib.conv_out_size.restype = i64
     lib.conv_out_size.argtypes = [i64, i, i, i, i]
     wp = ctypes.POINTER(ConvWindow)
@@ -100,9 +101,9 @@ def load_library():
     lib.conv_depthwise_fwd_window.restype = i
     lib.conv_depthwise_fwd_window.argtypes = [p, p, p, p] + [i] * 7 + [wp, i, i, p]
     lib.conv2d_nhwc_window_auto_variant.restype = i
-    lib.conv2d_nhwc_window_auto_variant.argtypes = [p, p] + [i] * 7 + [wp, i, i]
+    lib.conv2d_nhwc_window_auto_variant.argtypes = [p, p, p, p, p, p] + [i] * 7 + [wp, i, i]
     lib.conv_depthwise_window_auto_variant.restype = i
-    lib.conv_depthwise_window_auto_variant.argtypes = [i] * 7 + [wp]
+    lib.conv_depthwise_window_auto_variant.argtypes = [p, p, p, p] + [i] * 7 + [wp, i]
     lib.conv_im2col_nhwc.restype = i
     lib.conv_im2col_nhwc.argtypes = [p, p, p] + [i] * 6 + [wp, i, p]
     lib.conv_out_size_window.restype = i64
@@ -111,6 +112,8 @@ def load_library():
     lib.conv_status_str.argtypes = [i]
     lib.conv_copy_bytes.restype = i
     lib.conv_copy_bytes.argtypes = [p, p, i64, p]
+    lib.conv_copy_bytes_wide.restype = i
+    lib.conv_copy_bytes_wide.argtypes = [p, p, i64, p]
     _lib = lib
     return lib
 
@@ -292,29 +295,52 @@ def im2col_nhwc(x, KH: int, KW: int, stride=1, padding=0, dilation=1, out=None):
     return out
 
 
-def dense_variant_for(x, f, out_dtype=None, stride=1, padding=0, dilation=1, groups: int = 1) -> int:
-    """The variant CONV_VARIANT_AUTO launches for these tensors (host query)."""
+def dense_variant_for(x, f, out_dtype=None, stride=1, padding=0, dilation=1, groups: int = 1, bias=None,
+                      out=None) -> int:
+    """The variant CONV_VARIANT_AUTO launches for conv2d_nhwc with these
+    arguments (host query; -1 where the call would fail). Without `out` the
+    query describes the fresh output conv2d_nhwc allocates."""
     N, H, W, Cin = x.shape
     KH, KW, _, Cout = f.shape
     win = window(stride, padding, dilation, groups)
+    ydt = out.dtype if out is not None else (out_dtype or x.dtype)
     return int(load_library().conv2d_nhwc_window_auto_variant(
-        _strides_arr(x), x.data_ptr(), N, H, W, Cin, KH, KW, Cout, ctypes.byref(win), _dtype_code(x.dtype),
-        _dtype_code(out_dtype or x.dtype)))
+        x.data_ptr(), _strides_arr(x), f.data_ptr(), None if bias is None else bias.data_ptr(),
+        None if out is None else out.data_ptr(), None if out is None else _strides_arr(out),
+        N, H, W, Cin, KH, KW, Cout, ctypes.byref(win), _dtype_code(x.dtype), _dtype_code(ydt)))
 
 
-def depthwise_variant_for(shape_x, shape_w, stride=1, padding=0, dilation=1) -> int:
-    N, C, H, W = shape_x
-    Cout, KH, KW = shape_w
+def depthwise_variant_for(x, w, stride=1, padding=0, dilation=1, exact: bool = True, bias=None, out=None) -> int:
+    """The variant CONV_VARIANT_AUTO launches for conv_depthwise with these
+    tensors (host query; -1 where the call would fail). Without `out` the
+    query uses a stand-in output address past X (fresh allocations are
+    256-byte aligned; no alignment of Y is looked at)."""
+    N, C, H, W = x.shape
+    Cout, KH, KW = w.shape
     win = window(stride, padding, dilation)
-    return int(load_library().conv_depthwise_window_auto_variant(N, C, H, W, Cout // C, KH, KW, ctypes.byref(win)))
+    if out is not None:
+        y = out.data_ptr()
+    else:
+        # one past X, rounded up to 256 bytes: never overlapping X, w or bias
+        # as long as those were not allocated right behind X
+        y = (x.data_ptr() + x.numel() * 4 + 255) // 256 * 256
+        y = max(y, (w.data_ptr() + w.numel() * 4 + 255) // 256 * 256)
+        if bias is not None:
+            y = max(y, (bias.data_ptr() + bias.numel() * 4 + 255) // 256 * 256)
+    return int(load_library().conv_depthwise_window_auto_variant(
+        x.data_ptr(), w.data_ptr(), None if bias is None else bias.data_ptr(), y, N, C, H, W, Cout // C, KH, KW,
+        ctypes.byref(win), CONV_DW_EXACT if exact else CONV_DW_FAST))
 
 
-def copy_bytes(src, dst, nbytes: int | None = None):
-    """Plain streaming copy kernel (bandwidth / counter calibration)."""
+def copy_bytes(src, dst, nbytes: int | None = None, wide: bool = False):
+    """Streaming copy kernel (bandwidth / counter calibration): the plain
+    grid-stride copy, or with wide=True the one with eight loads in flight
+    per thread."""
     _require_gpu(src, dst)
     n = src.numel() * src.element_size() if nbytes is None else int(nbytes)
     if n > dst.numel() * dst.element_size() or n > src.numel() * src.element_size():
         raise ValueError("copy larger than a buffer")
-    _check(load_library().conv_copy_bytes(src.data_ptr(), dst.data_ptr(), n, _stream_ptr(src.device)),
-           "conv_copy_bytes")
+    fn = load_library().conv_copy_bytes_wide if wide else load_library().conv_copy_bytes
+    _check(fn(src.data_ptr(), dst.data_ptr(), n, _stream_ptr(src.device)),
+           "conv_copy_bytes_wide" if wide else "conv_copy_bytes")
     return dst

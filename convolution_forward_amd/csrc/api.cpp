@@ -21,13 +21,44 @@ struct Range {
     uintptr_t lo, hi;
 };
 
-Range strided_range(const void *base, const int64_t *dims, const int64_t *strides, int64_t esize)
+// Largest byte extent of a tensor the library addresses. Kernels form
+// element and byte offsets as int64 sums of index * stride terms, each no
+// larger than the extent, so every such sum stays far from overflow.
+constexpr int64_t MAX_EXTENT_BYTES = int64_t(1) << 60;
+
+// Bytes from the first to one past the last element of a strided 4-D
+// tensor (sizes >= 1, strides >= 0), or -1 when that exceeds
+// MAX_EXTENT_BYTES (or int64 arithmetic would overflow on the way).
+int64_t strided_extent(const int64_t *dims, const int64_t *strides, int64_t esize)
 {
     int64_t last = 0;
-    for (int d = 0; d < 4; ++d)
-        last += (dims[d] - 1) * strides[d];
+    for (int d = 0; d < 4; ++d) {
+        int64_t term;
+        if (__builtin_mul_overflow(dims[d] - 1, strides[d], &term) || __builtin_add_overflow(last, term, &last))
+            return -1;
+    }
+    int64_t bytes;
+    if (__builtin_add_overflow(last, (int64_t)1, &last) || __builtin_mul_overflow(last, esize, &bytes) ||
+        bytes > MAX_EXTENT_BYTES)
+        return -1;
+    return bytes;
+}
+
+Range strided_range(const void *base, int64_t extent_bytes)
+{
     uintptr_t lo = (uintptr_t)base;
-    return Range{lo, lo + (uintptr_t)((last + 1) * esize)};
+    return Range{lo, lo + (uintptr_t)extent_bytes};
+}
+
+// Bytes of a contiguous fp32 tensor of a*b*c*d elements (sizes >= 1), or -1
+// past MAX_EXTENT_BYTES.
+int64_t flat_bytes4(int64_t a, int64_t b, int64_t c, int64_t d)
+{
+    int64_t n;
+    if (__builtin_mul_overflow(a, b, &n) || __builtin_mul_overflow(n, c, &n) || __builtin_mul_overflow(n, d, &n) ||
+        __builtin_mul_overflow(n, (int64_t)4, &n) || n > MAX_EXTENT_BYTES)
+        return -1;
+    return n;
 }
 
 Range flat_range(const void *base, int64_t bytes)
@@ -83,6 +114,9 @@ conv_status check_dense_shape(const int64_t *x_strides, const int64_t *y_strides
         xs[1] = (int64_t)W * Cin;
         xs[0] = (int64_t)H * W * Cin;
     }
+    const int64_t xdims[4] = {N, H, W, Cin};
+    if (strided_extent(xdims, xs, dtype_size(x_dtype)) < 0)
+        return CONV_ERR_LAYOUT;
     if (y_strides) {
         for (int d = 0; d < 4; ++d) {
             if (!stride_ok(y_strides[d]))
@@ -101,6 +135,9 @@ conv_status check_dense_shape(const int64_t *x_strides, const int64_t *y_strides
         ys[1] = (int64_t)Wo * Cout;
         ys[0] = (int64_t)Ho * Wo * Cout;
     }
+    const int64_t ydims[4] = {N, Ho, Wo, Cout};
+    if (strided_extent(ydims, ys, dtype_size(y_dtype)) < 0)
+        return CONV_ERR_LAYOUT;
 
     p->X = nullptr;
     p->F = nullptr;
@@ -144,8 +181,9 @@ conv_status validate_dense(const void *X, const int64_t *x_strides, const void *
         return st;
     const int64_t xdims[4] = {N, H, W, Cin};
     const int64_t ydims[4] = {N, p->Ho, p->Wo, Cout};
-    const Range ry = strided_range(Y, ydims, p->ys, dtype_size(y_dtype));
-    if (overlaps(ry, strided_range(X, xdims, p->xs, dtype_size(x_dtype))) ||
+    // Both extents were checked by check_dense_shape.
+    const Range ry = strided_range(Y, strided_extent(ydims, p->ys, dtype_size(y_dtype)));
+    if (overlaps(ry, strided_range(X, strided_extent(xdims, p->xs, dtype_size(x_dtype)))) ||
         overlaps(ry, flat_range(F, (int64_t)KH * KW * (Cin / win.groups) * Cout * dtype_size(x_dtype))) ||
         (bias && overlaps(ry, flat_range(bias, (int64_t)Cout * 4))))
         return CONV_ERR_ALIAS;
@@ -194,6 +232,10 @@ conv_status check_dw_shape(int N, int C, int H, int W, int mult, int KH, int KW,
         return CONV_ERR_UNSUPPORTED;
     if ((int64_t)C * mult > INT_MAX)
         return CONV_ERR_UNSUPPORTED;
+    // Byte sizes of X, w and Y must be addressable (see MAX_EXTENT_BYTES).
+    if (flat_bytes4(N, C, H, W) < 0 || flat_bytes4(1, (int64_t)C * mult, KH, KW) < 0 ||
+        flat_bytes4(N, (int64_t)C * mult, Ho, Wo) < 0)
+        return CONV_ERR_UNSUPPORTED;
     p->X = nullptr;
     p->w = nullptr;
     p->bias = nullptr;
@@ -229,9 +271,10 @@ conv_status validate_dw(const float *X, const float *w, const float *bias, float
     if (st != CONV_OK)
         return st;
     const int64_t Cout = (int64_t)C * mult;
-    const Range ry = flat_range(Y, (int64_t)N * Cout * p->Ho * p->Wo * 4);
-    if (overlaps(ry, flat_range(X, (int64_t)N * C * H * W * 4)) ||
-        overlaps(ry, flat_range(w, Cout * KH * KW * 4)) || (bias && overlaps(ry, flat_range(bias, Cout * 4))))
+    // Every size was checked by check_dw_shape.
+    const Range ry = flat_range(Y, flat_bytes4(N, Cout, p->Ho, p->Wo));
+    if (overlaps(ry, flat_range(X, flat_bytes4(N, C, H, W))) || overlaps(ry, flat_range(w, flat_bytes4(1, Cout, KH, KW))) ||
+        (bias && overlaps(ry, flat_range(bias, Cout * 4))))
         return CONV_ERR_ALIAS;
     p->X = X;
     p->w = w;
@@ -336,23 +379,37 @@ conv_status conv2d_nhwc_fwd(const void *X, const int64_t *x_strides, const void 
                                    y_dtype, CONV_VARIANT_AUTO, stream);
 }
 
-int conv2d_nhwc_window_auto_variant(const int64_t *x_strides, const void *X, int N, int H, int W, int Cin, int KH,
-                                    int KW, int Cout, const conv_window *win, conv_dtype x_dtype,
-                                    conv_dtype y_dtype)
+int conv2d_nhwc_window_auto_variant(const void *X, const int64_t *x_strides, const void *F, const float *bias,
+                                    const void *Y, const int64_t *y_strides, int N, int H, int W, int Cin, int KH,
+                                    int KW, int Cout, const conv_window *win, conv_dtype x_dtype, conv_dtype y_dtype)
 {
-    DenseProblem p;
-    if (!win || check_dense_shape(x_strides, nullptr, N, H, W, Cin, KH, KW, Cout, *win, x_dtype, y_dtype, &p) !=
-                    CONV_OK)
+    if (!win || !X || !F)
         return -1;
-    p.X = X;    // only its alignment is looked at
+    DenseProblem p;
+    if (Y) {
+        // Exactly the checks of the call itself, aliasing included.
+        if (validate_dense(X, x_strides, F, bias, const_cast<void *>(Y), y_strides, N, H, W, Cin, KH, KW, Cout,
+                           *win, x_dtype, y_dtype, &p) != CONV_OK)
+            return -1;
+    } else {
+        // A fresh contiguous output, 256-byte aligned, that the caller has
+        // yet to allocate.
+        if (check_dense_shape(x_strides, nullptr, N, H, W, Cin, KH, KW, Cout, *win, x_dtype, y_dtype, &p) != CONV_OK)
+            return -1;
+        p.X = X;
+        p.F = F;
+        p.bias = bias;
+        p.Y = reinterpret_cast<void *>(uintptr_t(256));
+    }
     return dense_auto(p);
 }
 
-int conv2d_nhwc_auto_variant(const int64_t *x_strides, const void *X, int N, int H, int W, int Cin, int KH,
-                             int KW, int Cout, conv_dtype x_dtype, conv_dtype y_dtype)
+int conv2d_nhwc_auto_variant(const void *X, const int64_t *x_strides, const void *F, const float *bias, const void *Y,
+                             const int64_t *y_strides, int N, int H, int W, int Cin, int KH, int KW, int Cout,
+                             conv_dtype x_dtype, conv_dtype y_dtype)
 {
-    return conv2d_nhwc_window_auto_variant(x_strides, X, N, H, W, Cin, KH, KW, Cout, &PLAIN_WINDOW, x_dtype,
-                                           y_dtype);
+    return conv2d_nhwc_window_auto_variant(X, x_strides, F, bias, Y, y_strides, N, H, W, Cin, KH, KW, Cout,
+                                           &PLAIN_WINDOW, x_dtype, y_dtype);
 }
 
 conv_status conv_depthwise_fwd_window(const float *X, const float *w, const float *bias, float *Y, int N, int C,
@@ -401,22 +458,26 @@ conv_status conv_depthwise_fwd(const float *X, const float *w, const float *bias
                                       pad_w, dil_h, dil_w, mode, CONV_VARIANT_AUTO, stream);
 }
 
-int conv_depthwise_window_auto_variant(int N, int C, int H, int W, int multiplier, int KH, int KW,
-                                       const conv_window *win)
+int conv_depthwise_window_auto_variant(const float *X, const float *w, const float *bias, const float *Y, int N,
+                                       int C, int H, int W, int multiplier, int KH, int KW, const conv_window *win,
+                                       conv_dw_mode mode)
 {
+    if (!win || win->groups != 1)
+        return -1;
     DwProblem p;
-    if (!win || win->groups != 1 ||
-        check_dw_shape(N, C, H, W, multiplier, KH, KW, win->stride_h, win->stride_w, win->pad_top, win->pad_bottom,
-                       win->pad_left, win->pad_right, win->dil_h, win->dil_w, CONV_DW_EXACT, &p) != CONV_OK)
+    if (validate_dw(X, w, bias, const_cast<float *>(Y), N, C, H, W, multiplier, KH, KW, win->stride_h,
+                    win->stride_w, win->pad_top, win->pad_bottom, win->pad_left, win->pad_right, win->dil_h,
+                    win->dil_w, mode, &p) != CONV_OK)
         return -1;
     return dw_auto(p);
 }
 
-int conv_depthwise_auto_variant(int N, int C, int H, int W, int multiplier, int KH, int KW, int stride_h,
-                                int stride_w, int pad_h, int pad_w, int dil_h, int dil_w)
+int conv_depthwise_auto_variant(const float *X, const float *w, const float *bias, const float *Y, int N, int C,
+                                int H, int W, int multiplier, int KH, int KW, int stride_h, int stride_w, int pad_h,
+                                int pad_w, int dil_h, int dil_w, conv_dw_mode mode)
 {
     const conv_window win = {stride_h, stride_w, pad_h, pad_h, pad_w, pad_w, dil_h, dil_w, 1};
-    return conv_depthwise_window_auto_variant(N, C, H, W, multiplier, KH, KW, &win);
+    return conv_depthwise_window_auto_variant(X, w, bias, Y, N, C, H, W, multiplier, KH, KW, &win, mode);
 }
 
 conv_status conv_im2col_nhwc(const void *X, const int64_t *x_strides, void *cols, int N, int H, int W, int Cin,
@@ -432,8 +493,12 @@ conv_status conv_im2col_nhwc(const void *X, const int64_t *x_strides, void *cols
     if (st != CONV_OK)
         return st;
     const int64_t xdims[4] = {N, H, W, Cin};
-    const int64_t cols_bytes = (int64_t)N * d.Ho * d.Wo * KH * KW * Cin * dtype_size(dtype);
-    if (overlaps(flat_range(cols, cols_bytes), strided_range(X, xdims, d.xs, dtype_size(dtype))))
+    int64_t cols_bytes = 0;
+    if (__builtin_mul_overflow((int64_t)N * d.Ho, (int64_t)d.Wo * KH, &cols_bytes) ||
+        __builtin_mul_overflow(cols_bytes, (int64_t)KW * Cin * dtype_size(dtype), &cols_bytes) ||
+        cols_bytes > MAX_EXTENT_BYTES)
+        return CONV_ERR_UNSUPPORTED;
+    if (overlaps(flat_range(cols, cols_bytes), strided_range(X, strided_extent(xdims, d.xs, dtype_size(dtype)))))
         return CONV_ERR_ALIAS;
     Im2colProblem p;
     p.X = X;
@@ -469,6 +534,23 @@ conv_status conv_copy_bytes(const void *src, void *dst, int64_t bytes, void *str
     if (bytes == 0)
         return CONV_OK;
     return launched(launch_copy_bytes(src, dst, bytes, (hipStream_t)stream));
+}
+
+conv_status conv_copy_bytes_wide(const void *src, void *dst, int64_t bytes, void *stream)
+{
+    if (!src || !dst)
+        return CONV_ERR_NULL;
+    if (bytes < 0)
+        return CONV_ERR_NONPOSITIVE;
+    if ((uintptr_t)src % 16 != 0 || (uintptr_t)dst % 16 != 0 || bytes % 16 != 0)
+        return CONV_ERR_LAYOUT;
+    if (bytes > (int64_t(1) << 40))
+        return CONV_ERR_UNSUPPORTED;
+    if (overlaps(flat_range(src, bytes), flat_range(dst, bytes)))
+        return CONV_ERR_ALIAS;
+    if (bytes == 0)
+        return CONV_OK;
+    return launched(launch_copy_wide(src, dst, bytes, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace convfwd {
 
 // bf16 is the upper 16 bits of an IEEE binary32.
@@ -24,6 +26,27 @@ __device__ __forceinline__ float load_as_f32(const uint16_t *p) { return bf16_to
 
 __device__ __forceinline__ void store_from_f32(float *p, float v) { *p = v; }
 __device__ __forceinline__ void store_from_f32(uint16_t *p, float v) { *p = f32_to_bf16_rne(v); }
+
+// Raise kernel Kern's dynamic LDS limit to `bytes` on the current device
+// before its first launch there. Only a success is remembered (one bit per
+// device and kernel), so a failed attempt is made again by the next call;
+// later calls (graph capture included) then make no HIP call at all.
+template <auto Kern>
+hipError_t allow_lds(int bytes)
+{
+    static std::atomic<uint64_t> done{0};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    const uint64_t bit = dev >= 0 && dev < 64 ? uint64_t(1) << dev : 0;
+    if (bit && (done.load(std::memory_order_acquire) & bit))
+        return hipSuccess;
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(Kern), hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e == hipSuccess && bit)
+        done.fetch_or(bit, std::memory_order_acq_rel);
+    return e;
+}
 
 // Grid size for a grid-stride loop over `total` items: enough blocks to fill
 // the chip several times, never more than the work needs.

@@ -584,8 +584,7 @@ hipError_t launch_band(const BandArgs &a, dim3 grid, hipStream_t s)
 {
     auto kern = dense_band_mfma<KH, KW, CS, NR, SAUX, LS, OB, LR, LT>;
     constexpr size_t lds = BandShape<KH, KW, CS, NR, LS, OB, LR, LT>::LDS;
-    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    const hipError_t attr = allow_lds<dense_band_mfma<KH, KW, CS, NR, SAUX, LS, OB, LR, LT>>((int)lds);
     if (attr != hipSuccess)
         return attr;
     hipLaunchKernelGGL(kern, grid, dim3(BT), lds, s, a);

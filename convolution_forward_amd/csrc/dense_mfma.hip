@@ -701,10 +701,8 @@ hipError_t launch_inst(const RowArgs &a, dim3 grid, size_t lds, hipStream_t s)
         return hipErrorNotSupported;
     } else {
         auto kern = dense_rows_mfma<KH, KW, CS, BPW, MAXC, NR, S, OB>;
-        // Allow the full LDS once per instantiation (first launch, before any
-        // graph capture a caller may start later).
-        static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                                           hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES_MAX);
+        // Allow the full LDS (on the first launch on a device; see allow_lds).
+        const hipError_t attr = allow_lds<dense_rows_mfma<KH, KW, CS, BPW, MAXC, NR, S, OB>>(LDS_BYTES_MAX);
         if (attr != hipSuccess)
             return attr;
         hipLaunchKernelGGL(kern, grid, dim3(THREADS), lds, s, a);

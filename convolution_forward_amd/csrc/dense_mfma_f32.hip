@@ -400,8 +400,7 @@ hipError_t launch_inst_f32(const RowArgsF &a, dim3 grid, size_t lds, hipStream_t
 {
     constexpr int NR = band_rows_f32(KH);
     auto kern = dense_rows_mfma_f32<KH, KW, CS, BPW, MAXC, NR>;
-    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                                       hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES_MAX);
+    const hipError_t attr = allow_lds<dense_rows_mfma_f32<KH, KW, CS, BPW, MAXC, NR>>(LDS_BYTES_MAX);
     if (attr != hipSuccess)
         return attr;
     hipLaunchKernelGGL(kern, grid, dim3(THREADS), lds, s, a);

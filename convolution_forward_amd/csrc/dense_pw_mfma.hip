@@ -386,8 +386,7 @@ hipError_t launch_pw(const PwArgs &a, dim3 grid, hipStream_t s)
 {
     auto kern = dense_pw_mfma<CS, ROUNDS, OB, SLOTS, FFIRST>;
     constexpr size_t lds = PwShape<CS, OB, SLOTS, FFIRST>::LDS;
-    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    const hipError_t attr = allow_lds<dense_pw_mfma<CS, ROUNDS, OB, SLOTS, FFIRST>>((int)lds);
     if (attr != hipSuccess)
         return attr;
     hipLaunchKernelGGL(kern, grid, dim3(PT), lds, s, a);

@@ -77,7 +77,8 @@ struct Im2colProblem {
 
 hipError_t launch_im2col(const Im2colProblem &p, hipStream_t s);
 
-// Streaming copy used for bandwidth / counter calibration.
+// Streaming copies used for bandwidth / counter calibration.
 hipError_t launch_copy_bytes(const void *src, void *dst, int64_t bytes, hipStream_t s);
+hipError_t launch_copy_wide(const void *src, void *dst, int64_t bytes, hipStream_t s);
 
 }  // namespace convfwd

@@ -3,9 +3,11 @@
  *
  * A C ABI over hand-written HIP kernels. Every argument is a plain pointer or
  * integer; device buffers are owned by the caller. The library never
- * allocates device memory, keeps no global state and never synchronises: each
- * call validates its arguments on the host, then enqueues kernels on the
- * caller's stream and returns.
+ * allocates device memory and never synchronises: each call validates its
+ * arguments on the host, then enqueues kernels on the caller's stream and
+ * returns. Its only state is, per kernel and device, whether that kernel's
+ * dynamic LDS limit has been raised (hipFuncSetAttribute, done on the first
+ * launch there and remembered only once it succeeds); calls are thread-safe.
  *
  * Two operators:
  *
@@ -99,7 +101,8 @@ enum {
  *   stream     a hipStream_t (NULL = the default stream).
  *
  * Errors: CONV_ERR_NULL (X, F or Y NULL), CONV_ERR_NONPOSITIVE (any size
- * <= 0), CONV_ERR_SHAPE (KH > H or KW > W), CONV_ERR_DTYPE, CONV_ERR_LAYOUT,
+ * <= 0), CONV_ERR_SHAPE (KH > H or KW > W), CONV_ERR_DTYPE, CONV_ERR_LAYOUT
+ * (also when X's or Y's strided byte extent passes 2^60 bytes),
  * CONV_ERR_ALIAS (Y's byte range overlaps X, F or bias), CONV_ERR_HIP.
  * Y is fully overwritten on success; nothing accumulates into it.
  */
@@ -140,8 +143,9 @@ CONVFWD_API conv_status conv2d_nhwc_fwd_variant(const void *X, const int64_t *x_
  *
  * Errors: CONV_ERR_NULL (X, w or Y NULL), CONV_ERR_NONPOSITIVE (a size or
  * multiplier <= 0, stride or dilation < 1, padding < 0), CONV_ERR_SHAPE (an
- * output size <= 0), CONV_ERR_UNSUPPORTED (unknown mode, or a forced variant
- * that cannot take the shape), CONV_ERR_ALIAS (Y overlaps X, w or bias),
+ * output size <= 0), CONV_ERR_UNSUPPORTED (unknown mode, a tensor past 2^60
+ * bytes, or a forced variant that cannot take the shape), CONV_ERR_ALIAS (Y
+ * overlaps X, w or bias),
  * CONV_ERR_HIP.
  */
 CONVFWD_API conv_status conv_depthwise_fwd(const float *X, const float *w, const float *bias, float *Y, int N, int C,
@@ -238,19 +242,31 @@ CONVFWD_API conv_status conv_depthwise_fwd_window(const float *X, const float *w
 CONVFWD_API conv_status conv_im2col_nhwc(const void *X, const int64_t *x_strides, void *cols, int N, int H, int W,
                              int Cin, int KH, int KW, const conv_window *win, conv_dtype dtype, void *stream);
 
-/* Which variant CONV_VARIANT_AUTO would launch for these dense / depthwise
- * arguments (a CONV_VARIANT_* value), or -1 if the arguments are invalid.
- * Host-only; makes no HIP call. */
-CONVFWD_API int conv2d_nhwc_auto_variant(const int64_t *x_strides, const void *X, int N, int H, int W, int Cin,
-                             int KH, int KW, int Cout, conv_dtype x_dtype, conv_dtype y_dtype);
-CONVFWD_API int conv_depthwise_auto_variant(int N, int C, int H, int W, int multiplier, int KH, int KW, int stride_h,
-                                int stride_w, int pad_h, int pad_w, int dil_h, int dil_w);
-
-CONVFWD_API int conv2d_nhwc_window_auto_variant(const int64_t *x_strides, const void *X, int N, int H, int W,
-                                    int Cin, int KH, int KW, int Cout, const conv_window *win,
-                                    conv_dtype x_dtype, conv_dtype y_dtype);
-CONVFWD_API int conv_depthwise_window_auto_variant(int N, int C, int H, int W, int multiplier, int KH, int KW,
-                                       const conv_window *win);
+/*
+ * Which variant CONV_VARIANT_AUTO launches for exactly these arguments (a
+ * CONV_VARIANT_* value), or -1 where the call itself would return an error.
+ * Arguments are those of conv2d_nhwc_fwd_window / conv2d_nhwc_fwd and
+ * conv_depthwise_fwd_window / conv_depthwise_fwd, without variant and
+ * stream: the kernel choice looks at the pointers' alignment and the
+ * strides, so these are the pointers and strides the call will pass. For
+ * the dense queries Y may be NULL, meaning a fresh contiguous output on a
+ * 256-byte boundary that the caller is about to allocate (y_strides is then
+ * ignored). Host-only: no HIP call, nothing dereferenced.
+ */
+CONVFWD_API int conv2d_nhwc_window_auto_variant(const void *X, const int64_t *x_strides, const void *F,
+                                                const float *bias, const void *Y, const int64_t *y_strides, int N,
+                                                int H, int W, int Cin, int KH, int KW, int Cout,
+                                                const conv_window *win, conv_dtype x_dtype, conv_dtype y_dtype);
+CONVFWD_API int conv2d_nhwc_auto_variant(const void *X, const int64_t *x_strides, const void *F, const float *bias,
+                                         const void *Y, const int64_t *y_strides, int N, int H, int W, int Cin,
+                                         int KH, int KW, int Cout, conv_dtype x_dtype, conv_dtype y_dtype);
+CONVFWD_API int conv_depthwise_window_auto_variant(const float *X, const float *w, const float *bias, const float *Y,
+                                                   int N, int C, int H, int W, int multiplier, int KH, int KW,
+                                                   const conv_window *win, conv_dw_mode mode);
+CONVFWD_API int conv_depthwise_auto_variant(const float *X, const float *w, const float *bias, const float *Y, int N,
+                                            int C, int H, int W, int multiplier, int KH, int KW, int stride_h,
+                                            int stride_w, int pad_h, int pad_w, int dil_h, int dil_w,
+                                            conv_dw_mode mode);
 
 /* Output size along one axis: floor((in + 2*pad - (dil*(k-1)+1)) / stride) + 1
  * ("Convolution Is Wx+b Moving Across a Signal", section "Why 1D? Why 2D?").
@@ -270,6 +286,16 @@ CONVFWD_API const char *conv_status_str(conv_status s);
  * Errors: CONV_ERR_NULL, CONV_ERR_NONPOSITIVE (bytes < 0), CONV_ERR_ALIAS,
  * CONV_ERR_HIP. bytes == 0 enqueues nothing. */
 CONVFWD_API conv_status conv_copy_bytes(const void *src, void *dst, int64_t bytes, void *stream);
+
+/* The same copy with as many bytes in flight as the chip takes: each thread
+ * issues eight 16-byte loads before its first store, every workgroup is
+ * resident at once, and stores write through (device scope, streaming hint).
+ * It bounds from above what a kernel that must read and write these byte
+ * counts once can reach. src, dst and bytes must be multiples of 16
+ * (CONV_ERR_LAYOUT otherwise); bytes <= 2^40 (CONV_ERR_UNSUPPORTED);
+ * CONV_ERR_NULL, CONV_ERR_NONPOSITIVE, CONV_ERR_ALIAS, CONV_ERR_HIP as
+ * conv_copy_bytes. */
+CONVFWD_API conv_status conv_copy_bytes_wide(const void *src, void *dst, int64_t bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -141,21 +141,79 @@ def test_copy_errors(lib):
     assert lib.conv_copy_bytes(XA, YA, -1, None) == cf.CONV_ERR_NONPOSITIVE
     assert lib.conv_copy_bytes(XA, XA + 8, 16, None) == cf.CONV_ERR_ALIAS
     assert lib.conv_copy_bytes(XA, YA, 0, None) == cf.CONV_OK        # nothing enqueued
+    assert lib.conv_copy_bytes_wide(None, YA, 16, None) == cf.CONV_ERR_NULL
+    assert lib.conv_copy_bytes_wide(XA, YA, -16, None) == cf.CONV_ERR_NONPOSITIVE
+    assert lib.conv_copy_bytes_wide(XA, YA, 24, None) == cf.CONV_ERR_LAYOUT
+    assert lib.conv_copy_bytes_wide(XA + 8, YA, 16, None) == cf.CONV_ERR_LAYOUT
+    assert lib.conv_copy_bytes_wide(XA, XA + 16, 32, None) == cf.CONV_ERR_ALIAS
+    assert lib.conv_copy_bytes_wide(XA, YA, 0, None) == cf.CONV_OK
+
+
+def dq_shape(lib, N, C, H, W, m, KH, KW, sh, sw, ph, pw, dh, dw, X=XA):
+    return lib.conv_depthwise_auto_variant(X, FA, None, YA, N, C, H, W, m, KH, KW, sh, sw, ph, pw, dh, dw,
+                                           cf.CONV_DW_EXACT)
 
 
 def test_auto_variant_queries(lib):
-    assert lib.conv2d_nhwc_auto_variant(None, XA, 0, 8, 8, 3, 3, 3, 4, 0, 0) == -1
-    assert lib.conv2d_nhwc_auto_variant(None, XA, 2, 8, 8, 3, 3, 3, 4, 0, 0) in (cf.VARIANT_DIRECT, cf.VARIANT_TILED)
-    assert lib.conv_depthwise_auto_variant(1, 1, 3, 3, 1, 5, 5, 1, 1, 0, 0, 1, 1) == -1
+    q = lambda N=2, X=XA, F=FA, Y=YA, ys=None, xdt=0, ydt=0, C=3, O=4: lib.conv2d_nhwc_auto_variant(
+        X, None, F, None, Y, ys, N, 8, 8, C, 3, 3, O, xdt, ydt)
+    assert q(N=0) == -1
+    assert q(X=None) == -1 and q(F=None) == -1
+    assert q() in (cf.VARIANT_DIRECT, cf.VARIANT_TILED)
+    assert q(Y=XA + 8) == -1                               # the call would fail with CONV_ERR_ALIAS
+    assert dq_shape(lib, 1, 1, 3, 3, 1, 5, 5, 1, 1, 0, 0, 1, 1) == -1
     # Every measured depthwise workload runs on the LDS-tiled kernel.
     import workloads as wl
     for l in (wl.DW_5X5S2_EXACT, *wl.DW_SWEEP):
-        v = lib.conv_depthwise_auto_variant(l.N, l.C, l.H, l.W, l.mult, l.KH, l.KW, l.stride, l.stride,
-                                            l.pad, l.pad, l.dil, l.dil)
+        v = dq_shape(lib, l.N, l.C, l.H, l.W, l.mult, l.KH, l.KW, l.stride, l.stride, l.pad, l.pad, l.dil, l.dil)
         assert v == cf.VARIANT_TILED, l.name
+    # ... but not from an input that is not 16-byte aligned
+    l = wl.DW_5X5S2_EXACT
+    assert dq_shape(lib, l.N, l.C, l.H, l.W, 1, 5, 5, 2, 2, 2, 2, 1, 1, X=XA + 4) == cf.VARIANT_DIRECT
     # Shapes the tiled kernel does not take fall back to the direct kernel.
-    assert lib.conv_depthwise_auto_variant(2, 4, 11, 11, 3, 3, 3, 3, 3, 0, 0, 1, 1) == cf.VARIANT_DIRECT
-    assert lib.conv_depthwise_auto_variant(1, 2, 19, 23, 1, 3, 3, 1, 1, 2, 2, 2, 2) == cf.VARIANT_DIRECT
+    assert dq_shape(lib, 2, 4, 11, 11, 3, 3, 3, 3, 3, 0, 0, 1, 1) == cf.VARIANT_DIRECT
+    assert dq_shape(lib, 1, 2, 19, 23, 1, 3, 3, 1, 1, 2, 2, 2, 2) == cf.VARIANT_DIRECT
+
+
+def test_dense_query_sees_output_layout(lib):
+    """The dense query takes the call's own F, Y and Y strides: a bf16 3x3
+    layer runs tiled into an aligned, contiguous output and on the direct
+    kernel when Y (or F for fp32) is misaligned or Y's pixel stride breaks the
+    kernels' 16-byte pieces."""
+    BF = cf.CONV_BF16
+    ys = lambda *v: (ctypes.c_int64 * 4)(*v)
+    q = lambda Y=YA, y_strides=None, F=FA, dt=BF: lib.conv2d_nhwc_auto_variant(
+        XA, None, F, None, Y, y_strides, 2, 12, 12, 64, 3, 3, 64, dt, dt)
+    assert q() == cf.VARIANT_TILED
+    assert q(Y=None) == cf.VARIANT_TILED                      # a fresh output
+    assert q(Y=YA + 2) == cf.VARIANT_DIRECT                   # 2-byte aligned Y
+    assert q(y_strides=ys(10 * 10 * 68, 10 * 68, 68, 1)) == cf.VARIANT_DIRECT   # pixel stride 68 bf16
+    assert q(y_strides=ys(10 * 10 * 72, 10 * 72, 72, 1)) == cf.VARIANT_TILED    # pixel stride 72 bf16
+
+
+def test_extents_past_the_addressable_range(lib):
+    """Strided extents whose byte size overflows (or passes 2^60) are layout
+    errors, checked with overflow-safe arithmetic before anything else."""
+    big = (ctypes.c_int64 * 4)(1 << 40, 1 << 40, 1 << 40, 1)
+    n = 2 ** 31 - 1                                  # (n - 1) * 2^40 overflows int64
+    st = lib.conv2d_nhwc_fwd(XA, big, FA, None, YA, None, n, n, n, 8, 1, 1, 8, cf.CONV_BF16, cf.CONV_BF16, None)
+    assert st == cf.CONV_ERR_LAYOUT
+    # 2^20 * 2^40 * 2 bytes = 2^61 > 2^60 without overflowing int64
+    mid = (ctypes.c_int64 * 4)(1 << 40, 1 << 30, 8, 1)
+    st = lib.conv2d_nhwc_fwd(XA, mid, FA, None, YA, None, 2 ** 20 + 1, 4, 4, 8, 1, 1, 8, cf.CONV_BF16, cf.CONV_BF16,
+                             None)
+    assert st == cf.CONV_ERR_LAYOUT
+    ybig = (ctypes.c_int64 * 4)(1 << 40, 1 << 30, 8, 1)
+    st = lib.conv2d_nhwc_fwd(XA, None, FA, None, YA, ybig, 2 ** 20 + 1, 4, 4, 8, 1, 1, 8, cf.CONV_BF16,
+                             cf.CONV_BF16, None)
+    assert st == cf.CONV_ERR_LAYOUT
+    # contiguous, but N*H*W*Cin*2 bytes is far past 2^60
+    st = lib.conv2d_nhwc_fwd(XA, None, FA, None, YA, None, 2 ** 31 - 1, 2 ** 31 - 1, 2 ** 31 - 1, 8, 1, 1, 8,
+                             cf.CONV_BF16, cf.CONV_BF16, None)
+    assert st == cf.CONV_ERR_LAYOUT
+    st = lib.conv_depthwise_fwd(XA, FA, None, YA, 2 ** 31 - 1, 2 ** 31 - 1, 2 ** 20, 2 ** 20, 1, 3, 3, 1, 1, 1, 1,
+                                1, 1, cf.CONV_DW_EXACT, None)
+    assert st == cf.CONV_ERR_UNSUPPORTED
 
 
 def test_binding_rejects_cpu_tensors(lib):
@@ -220,13 +278,16 @@ def test_window_auto_variants(lib):
     point is routed like conv2d_nhwc_fwd."""
     W = cf.window
     q = lambda win, dt=cf.CONV_BF16, **k: lib.conv2d_nhwc_window_auto_variant(
-        None, XA, k.get("N", 2), k.get("H", 12), k.get("Wd", 12), 64, 3, 3, 64, ctypes.byref(win), dt, dt)
-    assert q(W()) == lib.conv2d_nhwc_auto_variant(None, XA, 2, 12, 12, 64, 3, 3, 64, cf.CONV_BF16, cf.CONV_BF16)
+        XA, None, FA, None, YA, None, k.get("N", 2), k.get("H", 12), k.get("Wd", 12), 64, 3, 3, 64, ctypes.byref(win),
+        dt, dt)
+    assert q(W()) == lib.conv2d_nhwc_auto_variant(XA, None, FA, None, YA, None, 2, 12, 12, 64, 3, 3, 64, cf.CONV_BF16,
+                                                  cf.CONV_BF16)
     assert q(W(groups=0)) == -1
     assert q(W(padding=1, dilation=2)) == cf.VARIANT_TILED
     assert q(W(padding=1, dilation=2), cf.CONV_F32) == cf.VARIANT_DIRECT
-    dq = lambda win: lib.conv_depthwise_window_auto_variant(8, 72, 56, 56, 1, 5, 5, ctypes.byref(win))
-    assert dq(W(stride=2, padding=2)) == lib.conv_depthwise_auto_variant(8, 72, 56, 56, 1, 5, 5, 2, 2, 2, 2, 1, 1)
+    dq = lambda win: lib.conv_depthwise_window_auto_variant(XA, FA, None, YA, 8, 72, 56, 56, 1, 5, 5,
+                                                            ctypes.byref(win), cf.CONV_DW_EXACT)
+    assert dq(W(stride=2, padding=2)) == dq_shape(lib, 8, 72, 56, 56, 1, 5, 5, 2, 2, 2, 2, 1, 1)
     assert dq(W(groups=2)) == -1
 
 

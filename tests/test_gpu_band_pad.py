@@ -45,7 +45,8 @@ def test_gpu_band_kernel_shapes(case):
     X = wl.random_tensor((N, H, W, C), seed).to(torch.bfloat16)
     F = (wl.random_tensor((3, 3, C // groups, O), seed + 1) * (1.0 / (9 * C / groups) ** 0.5)).to(torch.bfloat16)
     b = wl.random_tensor((O,), seed + 2) if has_bias else None
-    assert cf.dense_variant_for(X[:1].to(DEV), F.to(DEV), padding=pad, groups=groups) == cf.VARIANT_TILED
+    assert cf.dense_variant_for(X.to(DEV), F.to(DEV), padding=pad, groups=groups,
+                                bias=None if b is None else b.to(DEV)) == cf.VARIANT_TILED
     ref = oracle.conv2d_nhwc(X, F, bias=b, padding=pad, groups=groups)
     y = cf.conv2d_nhwc(X.to(DEV), F.to(DEV), bias=None if b is None else b.to(DEV), padding=pad, groups=groups)
     torch.cuda.synchronize()
@@ -120,7 +121,7 @@ def test_gpu_dw_padded_kernel_bitwise(case, mode):
     X = wl.random_tensor((N, C, H, W), seed)
     w = wl.random_tensor((C, K, K), seed + 1)
     b = wl.random_tensor((C,), seed + 2) if has_bias else None
-    assert cf.depthwise_variant_for((N, C, H, W), (C, K, K), s, p) == cf.VARIANT_TILED
+    assert cf.depthwise_variant_for(X.to(DEV), w.to(DEV), s, p) == cf.VARIANT_TILED
     ref = oracle.depthwise_nchw(X, w, bias=b, stride=s, padding=p, mode=mode)
     _assert_bits(_dw(X, w, b, s, p, mode), ref, mode)
 

@@ -123,11 +123,11 @@ TILED = [  # N, C, H, W, mult, K, stride, pad, bias
 @pytest.mark.parametrize("mode", ["exact", "fast"])
 def test_gpu_dw_tiled_shapes_bitwise(case, mode):
     N, C, H, W, m, K, s, p, has_bias = case
-    assert cf.depthwise_variant_for((N, C, H, W), (C * m, K, K), s, p) == cf.VARIANT_TILED
     seed = 6000 + TILED.index(case)
     X = wl.random_tensor((N, C, H, W), seed)
     w = wl.random_tensor((C * m, K, K), seed + 1)
     b = wl.random_tensor((C * m,), seed + 2) if has_bias else None
+    assert cf.depthwise_variant_for(X.to(DEV), w.to(DEV), s, p) == cf.VARIANT_TILED
     check(X, w, bias=b, stride=s, padding=p, mode=mode)
 
 

@@ -50,7 +50,7 @@ def test_gpu_depthwise_exact_input_past_2_31_elements():
     reps = 1190                                   # N = 9520: 2.149e9 elements (8.6 GB)
     X = Xb.to(DEV).repeat(reps, 1, 1, 1)
     assert X.numel() > 2 ** 31
-    assert cf.depthwise_variant_for(tuple(X.shape), tuple(w.shape), stride=2, padding=2) == cf.VARIANT_TILED
+    assert cf.depthwise_variant_for(X, w.to(DEV), stride=2, padding=2) == cf.VARIANT_TILED
     Y = cf.conv_depthwise(X, w.to(DEV), stride=2, padding=2, exact=True)
     torch.cuda.synchronize()
     del X

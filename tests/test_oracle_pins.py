@@ -52,13 +52,22 @@ def test_lecture_patch_rows(oracle_mod):
     np.testing.assert_array_equal(cols[0], g["patch_row_0"])
     np.testing.assert_array_equal(cols[1], g["patch_row_1"])
     assert cols.size == g["patch_values"] and A.size == g["input_values"]
-    # The overlapping patch view of section 4 (harness stride handling).
-    P = np.lib.stride_tricks.as_strided(A, shape=(4, 4, 3, 3), strides=A.strides + A.strides,
-                                        writeable=False)
-    assert list(P.strides) == g["patch_view_byte_strides"]
-    assert P[0, 0, 0, 1] == P[0, 1, 0, 0] == A[0, 1]
-    assert np.shares_memory(P, A) and not np.shares_memory(P.reshape(16, 9), A)
+    # Section 4's patch tensor from its index equation P[y, x, i, j] = A[y + i, x + j],
+    # built by gathering (a copy), must equal the patch rows.
+    yy, xx, ii, jj = np.meshgrid(np.arange(4), np.arange(4), np.arange(3), np.arange(3), indexing="ij")
+    P = A[yy + ii, xx + jj]
     np.testing.assert_array_equal(P.reshape(16, 9), cols)
+    # The same tensor as a view: the address of P[y,x,i,j] is (y+i)*row + (x+j)*col
+    # bytes, so its byte strides are (row, col, row, col) and neighbouring patches
+    # alias. numpy's sliding-window view is such a view; reshaping it to the
+    # patch matrix has to copy.
+    row, col = A.strides
+    assert [row, col, row, col] == g["patch_view_byte_strides"]
+    V = np.lib.stride_tricks.sliding_window_view(A, (3, 3))
+    assert list(V.strides) == g["patch_view_byte_strides"]
+    np.testing.assert_array_equal(V, P)
+    assert V[0, 0, 0, 1] == V[0, 1, 0, 0] == A[0, 1]
+    assert np.shares_memory(V, A) and not np.shares_memory(V.reshape(16, 9), A)
 
 
 def test_lecture_tile_view():
@@ -198,10 +207,12 @@ def test_k1_is_matmul_and_shifted_matmuls(oracle_mod, shape):
     F = random_tensor((K, K, C, O), seed + 1, integer_range=4).numpy()
     Y = oracle_mod.conv2d_nhwc(X, F)
     Ho, Wo = H - K + 1, W - K + 1
-    ref = np.zeros((N, Ho, Wo, O))
-    for i in range(K):
-        for j in range(K):
-            ref += X[:, i:i + Ho, j:j + Wo, :].astype(np.float64) @ F[i, j].astype(np.float64)
+    # The K^2 shifted copies of X stacked on a tap axis (shift (i, j) holds
+    # X[n, y+i, x+j, :]), each contracted over channels with F[i, j] and summed
+    # over the taps in one tensordot.
+    shifted = np.stack([np.roll(X, (-i, -j), axis=(1, 2))[:, :Ho, :Wo, :]
+                        for i in range(K) for j in range(K)], axis=3).astype(np.float64)
+    ref = np.tensordot(shifted, F.reshape(K * K, C, O).astype(np.float64), axes=([3, 4], [0, 1]))
     np.testing.assert_array_equal(Y, ref)
     np.testing.assert_array_equal(oracle_mod.conv2d_nhwc_im2col(X, F), Y)
     X1 = X.astype(np.float64).reshape(-1, C) @ F[0, 0].astype(np.float64)
@@ -273,12 +284,36 @@ def test_dense_translation_equivariance(oracle_mod):
     np.testing.assert_array_equal(Ys[:, 1:, 1:, :], Y[:, :-1, :-1, :])
 
 
-def test_dense_sampled_equals_full(oracle_mod):
-    X = random_tensor((2, 7, 6, 5), 41).numpy()
-    F = random_tensor((2, 3, 5, 3), 42).numpy()
-    Y = oracle_mod.conv2d_nhwc(X, F)
-    idx = np.array([0, 1, 17, 45, Y.size - 1], dtype=np.int64)
-    np.testing.assert_array_equal(oracle_mod.conv2d_nhwc_at(X, F, idx), Y.ravel()[idx])
+AT_CASES = [  # (N,H,W,Cin,KH,KW,Cout, stride, pad, dil, groups, bias)
+    (2, 7, 6, 5, 2, 3, 3, 1, 0, 1, 1, False),
+    (2, 9, 8, 4, 3, 3, 6, 1, 1, 1, 1, True),             # same padding
+    (1, 11, 10, 6, 3, 3, 4, 2, 1, 1, 2, True),           # stride 2, groups
+    (2, 10, 9, 4, 3, 2, 4, (2, 1), (2, 0), (2, 1), 4, False),  # unequal stride / pad, dilation, depthwise-like groups
+    (1, 1, 23, 6, 1, 3, 5, (1, 2), (0, 1), 1, 1, True),  # strided Conv1D stem shape
+    (3, 8, 8, 8, 5, 5, 8, 1, 2, 2, 8, False),            # 5x5 dilated depthwise as groups
+]
+
+
+@pytest.mark.parametrize("case", AT_CASES)
+def test_dense_sampled_equals_full(oracle_mod, case):
+    """The sampled form is the same sum at chosen indices: equal to the full
+    loops on every output index, over the stride / padding / dilation / groups
+    / bias superset, for indices given in any order and with repeats, and on
+    a strided (non-contiguous) input view."""
+    N, H, W, C, KH, KW, O, s, p, d, g, has_bias = case
+    seed = hash(case) & 0xFFFF
+    base = random_tensor((N, H, W, C + 3), seed).numpy()
+    X = base[..., 1:C + 1]
+    F = random_tensor((KH, KW, C // g, O), seed + 1).numpy()
+    b = random_tensor((O,), seed + 2).numpy() if has_bias else None
+    Y = oracle_mod.conv2d_nhwc(X, F, bias=b, stride=s, padding=p, dilation=d, groups=g)
+    idx = np.arange(Y.size, dtype=np.int64)
+    got = oracle_mod.conv2d_nhwc_at(X, F, idx, bias=b, stride=s, padding=p, dilation=d, groups=g)
+    np.testing.assert_array_equal(got, Y.ravel())
+    perm = np.random.default_rng(seed).permutation(Y.size)
+    perm = np.concatenate([perm, perm[:7]])
+    got = oracle_mod.conv2d_nhwc_at(X, F, perm, bias=b, stride=s, padding=p, dilation=d, groups=g)
+    np.testing.assert_array_equal(got, Y.ravel()[perm])
 
 
 # --- depthwise -----------------------------------------------------------------
