@@ -199,15 +199,17 @@ bool dense_tiled_supports(const DenseProblem &p)
 {
     if (p.xdt == CONV_BF16)
         return dense_mfma_bf16_supports(p) || dense_gemm_bf16_supports(p);
-    return plain_window(p) && dense_mfma_f32_supports(p);
+    return (plain_window(p) && dense_mfma_f32_supports(p)) || dense_gemm_f32_supports(p);
 }
 
-// bf16: the row kernel where its plan fits (band rows in LDS, filter in
-// registers), else the streamed-filter GEMM kernel.
+// The row kernel where its plan fits (band rows in LDS, filter in
+// registers; fp32 only for the lecture's plain window), else the GEMM
+// kernel of the operand type.
 hipError_t launch_dense_tiled(const DenseProblem &p, hipStream_t s)
 {
     if (p.xdt != CONV_BF16)
-        return launch_dense_mfma_f32(p, s);
+        return plain_window(p) && dense_mfma_f32_supports(p) ? launch_dense_mfma_f32(p, s)
+                                                              : launch_dense_gemm_f32(p, s);
     if (dense_mfma_bf16_supports(p))
         return launch_dense_mfma_bf16(p, s);
     return launch_dense_gemm_bf16(p, s);

@@ -56,6 +56,8 @@ bool dense_gemm_bf16_supports(const DenseProblem &p);
 hipError_t launch_dense_gemm_bf16(const DenseProblem &p, hipStream_t s);
 bool dense_mfma_f32_supports(const DenseProblem &p);
 hipError_t launch_dense_mfma_f32(const DenseProblem &p, hipStream_t s);
+bool dense_gemm_f32_supports(const DenseProblem &p);
+hipError_t launch_dense_gemm_f32(const DenseProblem &p, hipStream_t s);
 
 // Depthwise kernels.
 hipError_t launch_dw_direct(const DwProblem &p, hipStream_t s);

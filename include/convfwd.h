@@ -110,11 +110,12 @@ CONVFWD_API conv_status conv2d_nhwc_fwd(const void *X, const int64_t *x_strides,
                             void *Y, const int64_t *y_strides, int N, int H, int W, int Cin, int KH,
                             int KW, int Cout, conv_dtype x_dtype, conv_dtype y_dtype, void *stream);
 
-/* conv2d_nhwc_fwd with a forced kernel variant (CONV_VARIANT_*). The MFMA
- * variant needs bf16 or fp32 X with a 16-byte-aligned base and 16-byte
- * aligned pixel strides for bf16 (8 channels) or fp32 (4 channels), and
- * Cin and Cout that are multiples of 8 (bf16) or 4 (fp32); otherwise it
- * returns CONV_ERR_UNSUPPORTED. */
+/* conv2d_nhwc_fwd with a forced kernel variant (CONV_VARIANT_*). With bf16
+ * operands the MFMA variant needs X with a 16-byte-aligned base and 16-byte
+ * aligned pixel strides (8 channels), and Cin and Cout that are multiples of
+ * 8. With fp32 operands it takes any layout, window and channel count as
+ * long as N*Ho*Wo, KH*KW*Cin and Cout stay below 2^31 - 64. Otherwise it returns
+ * CONV_ERR_UNSUPPORTED. */
 CONVFWD_API conv_status conv2d_nhwc_fwd_variant(const void *X, const int64_t *x_strides, const void *F,
                                     const float *bias, void *Y, const int64_t *y_strides, int N, int H,
                                     int W, int Cin, int KH, int KW, int Cout, conv_dtype x_dtype,

@@ -272,10 +272,10 @@ def test_out_size_window(lib):
 
 
 def test_window_auto_variants(lib):
-    """bf16 windows of any shape go to a matrix-core kernel (a dilated window
-    to the streamed-filter GEMM); fp32 operands take the matrix cores only
-    for the lecture's plain window. The plain window through the window entry
-    point is routed like conv2d_nhwc_fwd."""
+    """Windows of any shape go to a matrix-core kernel (a dilated bf16 window
+    to the streamed-filter GEMM, an fp32 one to the fp32 GEMM kernel). The
+    plain window through the window entry point is routed like
+    conv2d_nhwc_fwd."""
     W = cf.window
     q = lambda win, dt=cf.CONV_BF16, **k: lib.conv2d_nhwc_window_auto_variant(
         XA, None, FA, None, YA, None, k.get("N", 2), k.get("H", 12), k.get("Wd", 12), 64, 3, 3, 64, ctypes.byref(win),
@@ -284,7 +284,8 @@ def test_window_auto_variants(lib):
                                                   cf.CONV_BF16)
     assert q(W(groups=0)) == -1
     assert q(W(padding=1, dilation=2)) == cf.VARIANT_TILED
-    assert q(W(padding=1, dilation=2), cf.CONV_F32) == cf.VARIANT_DIRECT
+    assert q(W(padding=1, dilation=2), cf.CONV_F32) == cf.VARIANT_TILED
+    assert q(W(stride=2, padding=3, groups=4), cf.CONV_F32) == cf.VARIANT_TILED
     dq = lambda win: lib.conv_depthwise_window_auto_variant(XA, FA, None, YA, 8, 72, 56, 56, 1, 5, 5,
                                                             ctypes.byref(win), cf.CONV_DW_EXACT)
     assert dq(W(stride=2, padding=2)) == dq_shape(lib, 8, 72, 56, 56, 1, 5, 5, 2, 2, 2, 2, 1, 1)

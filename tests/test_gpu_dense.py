@@ -79,8 +79,8 @@ def test_gpu_wxb_examples():
 def test_gpu_dense_tiny_f32(variant):
     w = wl.DENSE_TINY_F32
     X, F = wl.dense_inputs(w)
-    if not supported(X, F.to(DEV), variant):
-        pytest.skip("tiled variant does not take Cin=3")
+    # three input channels are zero-filled to the fp32 matrix cores' k granularity
+    assert cf.dense_variant_for(X.to(DEV), F.to(DEV)) == cf.VARIANT_TILED
     ref = oracle.conv2d_nhwc(X, F)
     Y = run(X, F, variant=variant)
     assert tuple(Y.shape) == (2, 6, 6, 4)

@@ -100,7 +100,8 @@ def test_gpu_dense_window(case, dtype):
         assert bf16_rounding_ok(Yb, ref, absref, KH * KW * C // groups)
         # the bf16 epilogue rounds the same fp32 accumulator to nearest-even
         assert torch.equal(Yb.cpu().view(torch.int16), Y.cpu().to(torch.bfloat16).view(torch.int16))
-    meant_tiled = (name.startswith("mfma") or name.startswith("gemm")) and dtype == "bf16"
+    # fp32 operands take the matrix cores in every window; bf16 in those named for them
+    meant_tiled = dtype == "f32" or name.startswith("mfma") or name.startswith("gemm")
     if meant_tiled:
         assert cf.dense_variant_for(X.to(DEV), F.to(DEV), bias=b.to(DEV), **kw) == cf.VARIANT_TILED
     # every variant that accepts the window gives the same contract; the
@@ -113,6 +114,52 @@ def test_gpu_dense_window(case, dtype):
             continue
         torch.cuda.synchronize()
         assert (max_rel_err(Yv, ref) <= F32_MAX_REL) if dtype == "f32" else (rms_rel_err(Yv, ref) <= 1e-3)
+
+
+F32_GEMM = [  # name, (N,H,W,Cin), (KH,KW,Cout), stride, padding, dilation, groups, (out channels, offset)
+    # groups of 48 output channels straddle the 64-channel tiles
+    ("groups_across_tiles", (2, 9, 11, 96), (3, 3, 144), 1, 1, 1, 3, None),
+    # three input channels (the small first layer), stride 2, Cout not a multiple of 4
+    ("cin3_stride2", (2, 33, 31, 3), (3, 3, 5), 2, 1, 1, 1, None),
+    ("cin3_7x7_s2_pad3", (1, 40, 36, 3), (7, 7, 64), 2, 3, 1, 1, None),
+    # one group per channel, through the dense entry point
+    ("channel_groups", (1, 10, 12, 16), (3, 3, 16), 1, 1, 1, 16, None),
+    # 2700 k values: many chunks and a ragged last one; pixel count ragged too
+    ("long_k", (1, 6, 7, 300), (3, 3, 70), 1, 1, 1, 1, None),
+    ("dilated_unequal", (2, 19, 23, 12), (3, 2, 20), (2, 1), (2, 0, 1, 1), (2, 3), 2, None),
+    # output into a channel slice: 16-byte aligned (vector stores) or not (scalar)
+    ("slice_aligned", (2, 9, 10, 20), (3, 3, 24), 1, 1, 1, 1, (40, 8)),
+    ("slice_unaligned", (2, 9, 10, 20), (3, 3, 24), 1, 1, 1, 1, (29, 3)),
+]
+
+
+@pytest.mark.parametrize("case", F32_GEMM, ids=lambda c: c[0])
+def test_gpu_dense_f32_gemm_kernel(case):
+    """fp32 windows the row kernel declines run on the fp32 matrix-core GEMM
+    kernel (AUTO picks it): every output against the oracle within the fp32
+    bar, nothing outside an output slice written."""
+    name, (N, H, W, C), (KH, KW, O), stride, padding, dilation, groups, slice_ = case
+    seed = 9700 + F32_GEMM.index(case)
+    X = wl.random_tensor((N, H, W, C), seed)
+    F = wl.random_tensor((KH, KW, C // groups, O), seed + 1) * (1.0 / (KH * KW * C / groups) ** 0.5)
+    b = wl.random_tensor((O,), seed + 2)
+    ref = dense_ref(X, F, b, stride, padding, dilation, groups)
+    kw = dict(stride=stride, padding=padding, dilation=dilation, groups=groups)
+    Xd, Fd, bd = X.to(DEV), F.to(DEV), b.to(DEV)
+    assert cf.dense_variant_for(Xd, Fd, bias=bd, **kw) == cf.VARIANT_TILED
+    if slice_ is None:
+        Y = cf.conv2d_nhwc(Xd, Fd, bias=bd, **kw)
+        torch.cuda.synchronize()
+    else:
+        total, off = slice_
+        buf = torch.full(ref.shape[:3] + (total,), float("nan"), device=DEV)
+        Y = buf[..., off:off + O]
+        cf.conv2d_nhwc(Xd, Fd, bias=bd, out=Y, **kw)
+        torch.cuda.synchronize()
+        outside = torch.cat([buf[..., :off], buf[..., off + O:]], dim=-1)
+        assert torch.isnan(outside).all()
+    assert tuple(Y.shape) == ref.shape
+    assert max_rel_err(Y, ref) <= F32_MAX_REL
 
 
 DW = [  # name, (N,C,H,W), mult, (KH,KW), stride, padding (t,b,l,r), dilation
