@@ -1,5 +1,5 @@
 // Dense NHWC cross-correlation, any window, as an implicit GEMM on matrix
-// cores with the filter streamed through LDS.
+// cores with both operands staged through LDS.
 //
 // Contract: "CMU DLSys Lecture 14: Convolutional Network Implementation",
 // sections 1 and 5 (Y = patch matrix times F.reshape(K*K*Cin, Cout), the
@@ -15,25 +15,33 @@
 // m = (n*Ho + y)*Wo + x, so any output shape tiles evenly.
 //
 // Work decomposition (one workgroup = 4 waves = 256 threads):
-//  * A tile is 256 output pixels x 64 output channels of one group. Wave w
-//    owns pixels 64w..64w+63 of the tile (four 16-pixel blocks) and all 64
-//    channels (four 16-channel column blocks): 16 accumulators, each MFMA
-//    reading 256 bytes of LDS for A and 256 bytes of memory for B.
-//  * The K axis runs over (tap i, tap j, 32-channel step), the lecture's
-//    (i, j, c) order. A chunk of KC steps of the filter slice
-//    F[i, j, c, o0:o0+64] is loaded coalesced, written to LDS in its natural
-//    layout (double buffered: the next chunk's loads are in flight while the
-//    current chunk is used) and read as A fragments with the gfx950
-//    transpose read ds_read_b64_tr_b16.
-//  * B fragments (8 channels of one pixel, 16 bytes per lane) are gathered
-//    straight from X for each step, one step ahead of use. Taps in the
-//    padding and pixels past the end use out-of-range buffer offsets, which
-//    load zeros without touching memory.
-//  * bf16 results are regrouped through the (by then idle) filter buffer:
-//    each wave parks its 64 pixels x 64 channels there, then eight lanes
-//    store each pixel's 128-byte row whole (stores of 8 bytes in 32-byte
-//    runs drain several times slower). fp32 results leave straight from the
-//    accumulators, 16 bytes per lane in 64-byte runs.
+//  * A tile is 64*BPW output pixels x 64 output channels of one group. Wave
+//    w owns the tile's 16-pixel blocks w*BPW .. w*BPW + BPW - 1 and all 64
+//    channels (four 16-channel column blocks): 4*BPW accumulators. BPW (2 to
+//    5) is chosen per launch so the tiles fill the compute units in as few
+//    rounds as possible.
+//  * The K axis runs over steps (32-channel slice, tap i, tap j): the taps
+//    of one slice follow each other, so they read input lines still in the
+//    caches (the sum is the same; only the fp32 rounding order differs from
+//    the lecture's (i, j, c)). Each step's operands are staged in LDS: the
+//    patch slice (the tile's pixels x 32 channels, 64 bytes a pixel) and the
+//    filter slice F[i, j, c:c+32, o0:o0+64] (4 KB), both with loads that
+//    write LDS directly (each wave instruction fills 1 KB contiguously; taps
+//    in the padding, pixels past the end and channels past Cin load zeros).
+//  * Steps go two to a stage through a ring of three stages: stage t + 2 is
+//    requested as stage t starts, so two stages are in flight while one is
+//    used. The waits are explicit counts: every memory instruction in the
+//    loop is unconditional (steps past the end load zeros into a free slot),
+//    so the number issued after stage t is a constant.
+//  * Filter fragments are read with the gfx950 transpose read, patch
+//    fragments with 16-byte reads; both are placed with an XOR swizzle so the
+//    16 lanes of a read hit distinct banks. All of a stage's fragment reads
+//    go out from one asm block that ends in its own wait (as intrinsics the
+//    transpose reads would be preceded by a wait for every load in flight).
+//  * bf16 results are regrouped through LDS (by then idle): each wave parks
+//    its pixels x 64 channels there, then eight lanes store each pixel's
+//    128-byte row whole. fp32 results leave straight from the accumulators,
+//    16 bytes per lane in 64-byte runs.
 #include <type_traits>
 
 #include "common.h"
@@ -50,18 +58,28 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int GT = 256;                 // threads per workgroup
-constexpr int GM = 256;                 // output pixels per tile
 constexpr int GN = 64;                  // output channels per tile
-constexpr int BLK = 4;                  // 16-pixel blocks per wave
 constexpr int NB = 4;                   // 16-channel column blocks per wave
-constexpr int KC = 4;                   // 32-channel steps per filter chunk
-constexpr int FP = GN + 8;              // LDS row pitch of a filter chunk (elements)
-constexpr int CHUNK_ELEMS = KC * 32 * FP;
-constexpr int FITEMS = KC * 32 * (GN / 8) / GT;   // 16-byte filter loads per thread per chunk
+constexpr int SPS = 2;                  // steps per stage
+constexpr int NSTAGE = 3;               // stages in the LDS ring
+constexpr int FSTEP = 32 * GN * 2;      // filter bytes per step
 constexpr int OPITCH = GN * 2 + 16;     // LDS pitch of one pixel of a wave's bf16 output patch (bytes)
-static_assert(GT / 64 * 64 * OPITCH <= 2 * CHUNK_ELEMS * 2, "output patches fit in the filter buffer");
 constexpr uint32_t OOB = 0x80000000u;
 constexpr int BUF_WORD3 = 0x00020000;
+constexpr int LDS_MAX = 160 * 1024;
+
+template <int BPW>
+struct GShape {
+    static constexpr int M = 64 * BPW;                  // pixels per tile
+    static constexpr int XSTEP = M * 64;                // patch bytes per step
+    static constexpr int STEP = XSTEP + FSTEP;
+    static constexpr int STAGE = SPS * STEP;
+    static constexpr int LDS = NSTAGE * STAGE;
+    static constexpr int LOADS = SPS * (BPW + 1);       // loads per thread per stage
+    static_assert(LDS <= LDS_MAX, "LDS");
+    static_assert(4 * 16 * BPW * OPITCH <= LDS, "output patches fit in the ring");
+    static_assert(LOADS < 64, "vmcnt holds 6 bits");
+};
 
 struct FastDivG {
     uint32_t m, s;
@@ -77,18 +95,175 @@ FastDivG make_fastdiv_g(uint32_t d)
 
 __device__ __forceinline__ uint32_t fdiv_g(uint32_t n, FastDivG f) { return (__umulhi(n, f.m) + n) >> f.s; }
 
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt holds 6 bits");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Physical 16-byte chunk of logical chunk c in row k of a staged filter
+// slice (rows of 128 bytes): the 8 rows that one half-wave's transpose read
+// touches fall in 8 distinct pairs of bank groups. (Patch pixels P, 64
+// bytes, keep logical chunk c at c ^ ((P >> 2) & 3): the 16 pixels of a
+// fragment read fall in 16 distinct bank groups.)
+__host__ __device__ constexpr int fswz(int k) { return (((k >> 1) & 1) << 1) | (((k >> 3) & 1) << 2); }
+
+// Every fragment read of one stage (two steps): for each step the four
+// filter fragments (two transposed 8-byte reads each, at +0 and +512 bytes
+// from the column block's base) and the BPW patch fragments (16-byte reads
+// 1 KB apart); step 1 sits STEP bytes after step 0. Outputs are
+// early-clobber so no read lands in an address register still to be used.
+template <int BPW>
+__device__ __forceinline__ void stage_reads(const uint32_t (&abase)[4], uint32_t xbase, i16x4 (&a)[2][4][2],
+                                            u32x4 (&b)[2][BPW]);
+
+template <>
+__device__ __forceinline__ void stage_reads<2>(const uint32_t (&abase)[4], uint32_t xbase, i16x4 (&a)[2][4][2],
+                                                 u32x4 (&b)[2][2])
+{
+    asm volatile("ds_read_b64_tr_b16 %0, %20 offset:0\n\t"
+                 "ds_read_b64_tr_b16 %1, %20 offset:512\n\t"
+                 "ds_read_b64_tr_b16 %2, %21 offset:0\n\t"
+                 "ds_read_b64_tr_b16 %3, %21 offset:512\n\t"
+                 "ds_read_b64_tr_b16 %4, %22 offset:0\n\t"
+                 "ds_read_b64_tr_b16 %5, %22 offset:512\n\t"
+                 "ds_read_b64_tr_b16 %6, %23 offset:0\n\t"
+                 "ds_read_b64_tr_b16 %7, %23 offset:512\n\t"
+                 "ds_read_b128 %16, %24 offset:0\n\t"
+                 "ds_read_b128 %17, %24 offset:1024\n\t"
+                 "ds_read_b64_tr_b16 %8, %20 offset:12288\n\t"
+                 "ds_read_b64_tr_b16 %9, %20 offset:12800\n\t"
+                 "ds_read_b64_tr_b16 %10, %21 offset:12288\n\t"
+                 "ds_read_b64_tr_b16 %11, %21 offset:12800\n\t"
+                 "ds_read_b64_tr_b16 %12, %22 offset:12288\n\t"
+                 "ds_read_b64_tr_b16 %13, %22 offset:12800\n\t"
+                 "ds_read_b64_tr_b16 %14, %23 offset:12288\n\t"
+                 "ds_read_b64_tr_b16 %15, %23 offset:12800\n\t"
+                 "ds_read_b128 %18, %24 offset:12288\n\t"
+                 "ds_read_b128 %19, %24 offset:13312\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(a[0][0][0]), "=&v"(a[0][0][1]), "=&v"(a[0][1][0]), "=&v"(a[0][1][1]), "=&v"(a[0][2][0]), "=&v"(a[0][2][1]), "=&v"(a[0][3][0]), "=&v"(a[0][3][1]), "=&v"(a[1][0][0]), "=&v"(a[1][0][1]), "=&v"(a[1][1][0]), "=&v"(a[1][1][1]), "=&v"(a[1][2][0]), "=&v"(a[1][2][1]), "=&v"(a[1][3][0]), "=&v"(a[1][3][1]), "=&v"(b[0][0]), "=&v"(b[0][1]), "=&v"(b[1][0]), "=&v"(b[1][1])
+                 : "v"(abase[0]), "v"(abase[1]), "v"(abase[2]), "v"(abase[3]), "v"(xbase)
+                 : "memory");
+}
+
+template <>
+__device__ __forceinline__ void stage_reads<3>(const uint32_t (&abase)[4], uint32_t xbase, i16x4 (&a)[2][4][2],
+                                                 u32x4 (&b)[2][3])
+{
+    asm volatile("ds_read_b64_tr_b16 %0, %22 offset:0\n\t"
+                 "ds_read_b64_tr_b16 %1, %22 offset:512\n\t"
+                 "ds_read_b64_tr_b16 %2, %23 offset:0\n\t"
+                 "ds_read_b64_tr_b16 %3, %23 offset:512\n\t"
+                 "ds_read_b64_tr_b16 %4, %24 offset:0\n\t"
+                 "ds_read_b64_tr_b16 %5, %24 offset:512\n\t"
+                 "ds_read_b64_tr_b16 %6, %25 offset:0\n\t"
+                 "ds_read_b64_tr_b16 %7, %25 offset:512\n\t"
+                 "ds_read_b128 %16, %26 offset:0\n\t"
+                 "ds_read_b128 %17, %26 offset:1024\n\t"
+                 "ds_read_b128 %18, %26 offset:2048\n\t"
+                 "ds_read_b64_tr_b16 %8, %22 offset:16384\n\t"
+                 "ds_read_b64_tr_b16 %9, %22 offset:16896\n\t"
+                 "ds_read_b64_tr_b16 %10, %23 offset:16384\n\t"
+                 "ds_read_b64_tr_b16 %11, %23 offset:16896\n\t"
+                 "ds_read_b64_tr_b16 %12, %24 offset:16384\n\t"
+                 "ds_read_b64_tr_b16 %13, %24 offset:16896\n\t"
+                 "ds_read_b64_tr_b16 %14, %25 offset:16384\n\t"
+                 "ds_read_b64_tr_b16 %15, %25 offset:16896\n\t"
+                 "ds_read_b128 %19, %26 offset:16384\n\t"
+                 "ds_read_b128 %20, %26 offset:17408\n\t"
+                 "ds_read_b128 %21, %26 offset:18432\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(a[0][0][0]), "=&v"(a[0][0][1]), "=&v"(a[0][1][0]), "=&v"(a[0][1][1]), "=&v"(a[0][2][0]), "=&v"(a[0][2][1]), "=&v"(a[0][3][0]), "=&v"(a[0][3][1]), "=&v"(a[1][0][0]), "=&v"(a[1][0][1]), "=&v"(a[1][1][0]), "=&v"(a[1][1][1]), "=&v"(a[1][2][0]), "=&v"(a[1][2][1]), "=&v"(a[1][3][0]), "=&v"(a[1][3][1]), "=&v"(b[0][0]), "=&v"(b[0][1]), "=&v"(b[0][2]), "=&v"(b[1][0]), "=&v"(b[1][1]), "=&v"(b[1][2])
+                 : "v"(abase[0]), "v"(abase[1]), "v"(abase[2]), "v"(abase[3]), "v"(xbase)
+                 : "memory");
+}
+
+template <>
+__device__ __forceinline__ void stage_reads<4>(const uint32_t (&abase)[4], uint32_t xbase, i16x4 (&a)[2][4][2],
+                                                 u32x4 (&b)[2][4])
+{
+    asm volatile("ds_read_b64_tr_b16 %0, %24 offset:0\n\t"
+                 "ds_read_b64_tr_b16 %1, %24 offset:512\n\t"
+                 "ds_read_b64_tr_b16 %2, %25 offset:0\n\t"
+                 "ds_read_b64_tr_b16 %3, %25 offset:512\n\t"
+                 "ds_read_b64_tr_b16 %4, %26 offset:0\n\t"
+                 "ds_read_b64_tr_b16 %5, %26 offset:512\n\t"
+                 "ds_read_b64_tr_b16 %6, %27 offset:0\n\t"
+                 "ds_read_b64_tr_b16 %7, %27 offset:512\n\t"
+                 "ds_read_b128 %16, %28 offset:0\n\t"
+                 "ds_read_b128 %17, %28 offset:1024\n\t"
+                 "ds_read_b128 %18, %28 offset:2048\n\t"
+                 "ds_read_b128 %19, %28 offset:3072\n\t"
+                 "ds_read_b64_tr_b16 %8, %24 offset:20480\n\t"
+                 "ds_read_b64_tr_b16 %9, %24 offset:20992\n\t"
+                 "ds_read_b64_tr_b16 %10, %25 offset:20480\n\t"
+                 "ds_read_b64_tr_b16 %11, %25 offset:20992\n\t"
+                 "ds_read_b64_tr_b16 %12, %26 offset:20480\n\t"
+                 "ds_read_b64_tr_b16 %13, %26 offset:20992\n\t"
+                 "ds_read_b64_tr_b16 %14, %27 offset:20480\n\t"
+                 "ds_read_b64_tr_b16 %15, %27 offset:20992\n\t"
+                 "ds_read_b128 %20, %28 offset:20480\n\t"
+                 "ds_read_b128 %21, %28 offset:21504\n\t"
+                 "ds_read_b128 %22, %28 offset:22528\n\t"
+                 "ds_read_b128 %23, %28 offset:23552\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(a[0][0][0]), "=&v"(a[0][0][1]), "=&v"(a[0][1][0]), "=&v"(a[0][1][1]), "=&v"(a[0][2][0]), "=&v"(a[0][2][1]), "=&v"(a[0][3][0]), "=&v"(a[0][3][1]), "=&v"(a[1][0][0]), "=&v"(a[1][0][1]), "=&v"(a[1][1][0]), "=&v"(a[1][1][1]), "=&v"(a[1][2][0]), "=&v"(a[1][2][1]), "=&v"(a[1][3][0]), "=&v"(a[1][3][1]), "=&v"(b[0][0]), "=&v"(b[0][1]), "=&v"(b[0][2]), "=&v"(b[0][3]), "=&v"(b[1][0]), "=&v"(b[1][1]), "=&v"(b[1][2]), "=&v"(b[1][3])
+                 : "v"(abase[0]), "v"(abase[1]), "v"(abase[2]), "v"(abase[3]), "v"(xbase)
+                 : "memory");
+}
+
+template <>
+__device__ __forceinline__ void stage_reads<5>(const uint32_t (&abase)[4], uint32_t xbase, i16x4 (&a)[2][4][2],
+                                                 u32x4 (&b)[2][5])
+{
+    asm volatile("ds_read_b64_tr_b16 %0, %26 offset:0\n\t"
+                 "ds_read_b64_tr_b16 %1, %26 offset:512\n\t"
+                 "ds_read_b64_tr_b16 %2, %27 offset:0\n\t"
+                 "ds_read_b64_tr_b16 %3, %27 offset:512\n\t"
+                 "ds_read_b64_tr_b16 %4, %28 offset:0\n\t"
+                 "ds_read_b64_tr_b16 %5, %28 offset:512\n\t"
+                 "ds_read_b64_tr_b16 %6, %29 offset:0\n\t"
+                 "ds_read_b64_tr_b16 %7, %29 offset:512\n\t"
+                 "ds_read_b128 %16, %30 offset:0\n\t"
+                 "ds_read_b128 %17, %30 offset:1024\n\t"
+                 "ds_read_b128 %18, %30 offset:2048\n\t"
+                 "ds_read_b128 %19, %30 offset:3072\n\t"
+                 "ds_read_b128 %20, %30 offset:4096\n\t"
+                 "ds_read_b64_tr_b16 %8, %26 offset:24576\n\t"
+                 "ds_read_b64_tr_b16 %9, %26 offset:25088\n\t"
+                 "ds_read_b64_tr_b16 %10, %27 offset:24576\n\t"
+                 "ds_read_b64_tr_b16 %11, %27 offset:25088\n\t"
+                 "ds_read_b64_tr_b16 %12, %28 offset:24576\n\t"
+                 "ds_read_b64_tr_b16 %13, %28 offset:25088\n\t"
+                 "ds_read_b64_tr_b16 %14, %29 offset:24576\n\t"
+                 "ds_read_b64_tr_b16 %15, %29 offset:25088\n\t"
+                 "ds_read_b128 %21, %30 offset:24576\n\t"
+                 "ds_read_b128 %22, %30 offset:25600\n\t"
+                 "ds_read_b128 %23, %30 offset:26624\n\t"
+                 "ds_read_b128 %24, %30 offset:27648\n\t"
+                 "ds_read_b128 %25, %30 offset:28672\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(a[0][0][0]), "=&v"(a[0][0][1]), "=&v"(a[0][1][0]), "=&v"(a[0][1][1]), "=&v"(a[0][2][0]), "=&v"(a[0][2][1]), "=&v"(a[0][3][0]), "=&v"(a[0][3][1]), "=&v"(a[1][0][0]), "=&v"(a[1][0][1]), "=&v"(a[1][1][0]), "=&v"(a[1][1][1]), "=&v"(a[1][2][0]), "=&v"(a[1][2][1]), "=&v"(a[1][3][0]), "=&v"(a[1][3][1]), "=&v"(b[0][0]), "=&v"(b[0][1]), "=&v"(b[0][2]), "=&v"(b[0][3]), "=&v"(b[0][4]), "=&v"(b[1][0]), "=&v"(b[1][1]), "=&v"(b[1][2]), "=&v"(b[1][3]), "=&v"(b[1][4])
+                 : "v"(abase[0]), "v"(abase[1]), "v"(abase[2]), "v"(abase[3]), "v"(xbase)
+                 : "memory");
+}
+
 struct GemmArgs {
     const uint16_t *X;
     const uint16_t *F;
     const float *bias;
     void *Y;
     int64_t xs0, xs1, xs2, ys0, ys1, ys2;
-    int H, W, Ho, Wo, KW;
+    int H, W, Ho, Wo, KH, KW;
     int Cin, Cout;          // channels of one group
     int f_ld;               // F row length (output channels of all groups)
     int sh, sw, pt, pl, dh, dw;
-    int cs_steps;           // 32-channel steps per tap
-    int ksteps;             // KH * KW * cs_steps
+    int ksteps;             // KH * KW * (32-channel slices)
+    int nstages;            // ceil(ksteps / SPS)
     int m_total;            // N * Ho * Wo
     int n_tiles;            // 64-channel tiles per group
     int nt_all;             // n_tiles * groups: channel tiles per pixel tile
@@ -97,11 +272,12 @@ struct GemmArgs {
     FastDivG div_wo, div_ho;
 };
 
-template <bool OUT_BF16>
+template <int BPW, bool OUT_BF16>
 __global__ __launch_bounds__(GT) void dense_gemm_mfma(GemmArgs a)
 {
+    using S = GShape<BPW>;
     constexpr int ESZ = OUT_BF16 ? 2 : 4;
-    __shared__ __align__(16) uint16_t fbuf[2][CHUNK_ELEMS];
+    extern __shared__ __align__(16) uint8_t ring[];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -118,146 +294,152 @@ __global__ __launch_bounds__(GT) void dense_gemm_mfma(GemmArgs a)
     const int grp = nt / a.n_tiles;
     const int o0 = (nt - grp * a.n_tiles) * GN;
     const int xc0 = grp * a.Cin, oc0 = grp * a.Cout;
-
-    // This lane's pixel in each of the wave's four blocks.
-    int iy0[BLK], ix0[BLK], yo[BLK], xo[BLK];
-    uint32_t nb0[BLK];
-    bool mok[BLK];
-#pragma unroll
-    for (int b = 0; b < BLK; ++b) {
-        const int m = mt * GM + wave * 64 + b * 16 + r;
-        mok[b] = m < a.m_total;
-        const uint32_t mm = mok[b] ? (uint32_t)m : 0u;
-        const uint32_t ny = fdiv_g(mm, a.div_wo);
-        xo[b] = (int)(mm - ny * (uint32_t)a.Wo);
-        const uint32_t n = fdiv_g(ny, a.div_ho);
-        yo[b] = (int)(ny - n * (uint32_t)a.Ho);
-        nb0[b] = n;
-        iy0[b] = yo[b] * a.sh - a.pt;
-        ix0[b] = xo[b] * a.sw - a.pl;
-    }
+    const int m0 = mt * S::M;
 
     const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t *>(a.X), 0, (int)a.x_records, BUF_WORD3);
     const __amdgpu_buffer_rsrc_t fr = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t *>(a.F), 0, (int)a.f_records, BUF_WORD3);
 
-    // Filter chunk q: items it -> (8-channel output group og fastest, then
-    // row kk*32 + c of the chunk).
-    auto chunk_load = [&](int q, u32x4 (&fv)[FITEMS]) __attribute__((always_inline)) {
+    // Patch loads: load v of wave w fills tile pixels 16*(4v + w) ..+15,
+    // lane L taking pixel 16*(4v + w) + L/4 and stored chunk L % 4, which
+    // holds logical chunk (L % 4) ^ ((pixel / 4) % 4) (8 channels).
+    const int xchunk = (lane & 3) ^ ((lane >> 4) & 3);
+    int xb0[BPW], iy0[BPW], ix0[BPW];
+    bool mok[BPW];
 #pragma unroll
-        for (int t = 0; t < FITEMS; ++t) {
-            const int it = tid + t * GT;
-            const int og = it & 7;
-            const int row = it >> 3;
-            const int ks = q * KC + row / 32;
-            const int c = row % 32;
-            const int tap = ks / a.cs_steps;
-            const int cc = (ks - tap * a.cs_steps) * 32 + c;
-            const int o = o0 + og * 8;
-            const bool ok = ks < a.ksteps && cc < a.Cin && o < a.Cout;
-            fv[t] = __builtin_amdgcn_raw_buffer_load_b128(
-                fr, ok ? (uint32_t)((((int64_t)tap * a.Cin + cc) * a.f_ld + oc0 + o) * 2) : OOB, 0, 0);
+    for (int v = 0; v < BPW; ++v) {
+        const int m = m0 + 16 * (4 * v + wave) + (lane >> 2);
+        mok[v] = m < a.m_total;
+        const uint32_t mm = mok[v] ? (uint32_t)m : 0u;
+        const uint32_t ny = fdiv_g(mm, a.div_wo);
+        const int x = (int)(mm - ny * (uint32_t)a.Wo);
+        const uint32_t n = fdiv_g(ny, a.div_ho);
+        const int y = (int)(ny - n * (uint32_t)a.Ho);
+        xb0[v] = (int)(n * (uint32_t)a.xs0) + xc0 + 8 * xchunk;
+        iy0[v] = y * a.sh - a.pt;
+        ix0[v] = x * a.sw - a.pl;
+    }
+    // Filter loads: wave w fills rows 8w .. 8w+7 of a step's slice, lane L
+    // row 8w + L/8, stored chunk L % 8 (logical chunk (L % 8) ^ fswz(row)).
+    const int frow = 8 * wave + (lane >> 3);
+    const int fcol = o0 + 8 * ((lane & 7) ^ fswz(frow));
+    const bool fcol_ok = fcol < a.Cout;
+
+    // The step whose loads go out next: tap (li, lj), channel slice lcs.
+    int lks = 0, lcs = 0, li = 0, lj = 0;
+    auto issue_step = [&](uint8_t *dst) __attribute__((always_inline)) {
+        const bool kok = lks < a.ksteps;
+        const int c = lcs * 32;
+#pragma unroll
+        for (int v = 0; v < BPW; ++v) {
+            const int iy = iy0[v] + li * a.dh;
+            const int ix = ix0[v] + lj * a.dw;
+            const bool ok = kok && mok[v] && (unsigned)iy < (unsigned)a.H && (unsigned)ix < (unsigned)a.W &&
+                            c + 8 * xchunk < a.Cin;
+            const uint32_t off =
+                ok ? ((uint32_t)xb0[v] + (uint32_t)iy * (uint32_t)a.xs1 + (uint32_t)ix * (uint32_t)a.xs2 + (uint32_t)c) * 2u
+                   : OOB;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                xr, (__attribute__((address_space(3))) void *)(dst + 1024 * (4 * v + wave)), 16, off, 0, 0, 0);
+        }
+        {
+            const int tap = li * a.KW + lj;
+            const bool ok = kok && fcol_ok && c + frow < a.Cin;
+            const uint32_t off = ok ? (uint32_t)((((int64_t)tap * a.Cin + c + frow) * a.f_ld + oc0 + fcol) * 2) : OOB;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                fr, (__attribute__((address_space(3))) void *)(dst + S::XSTEP + 1024 * wave), 16, off, 0, 0, 0);
+        }
+        // Next step: tap column, then tap row, then channel slice (the taps
+        // of one slice read neighbouring input lines while they are cached).
+        ++lks;
+        if (++lj == a.KW) {
+            lj = 0;
+            if (++li == a.KH) {
+                li = 0;
+                ++lcs;
+            }
         }
     };
-    auto chunk_store = [&](int buf, const u32x4 (&fv)[FITEMS]) __attribute__((always_inline)) {
+    auto issue_stage = [&](int t) __attribute__((always_inline)) {
+        uint8_t *dst = ring + (t % NSTAGE) * S::STAGE;
 #pragma unroll
-        for (int t = 0; t < FITEMS; ++t) {
-            const int it = tid + t * GT;
-            *reinterpret_cast<u32x4 *>(&fbuf[buf][(it >> 3) * FP + (it & 7) * 8]) = fv[t];
-        }
-    };
-    // B fragments of step ks for the four blocks.
-    auto b_load = [&](int ks, bf16x8 (&xb)[BLK]) __attribute__((always_inline)) {
-        const int tap = ks / a.cs_steps;
-        const int cs = ks - tap * a.cs_steps;
-        const int i = tap / a.KW;
-        const int j = tap - i * a.KW;
-        const int c = cs * 32 + g * 8;
-#pragma unroll
-        for (int b = 0; b < BLK; ++b) {
-            const int iy = iy0[b] + i * a.dh;
-            const int ix = ix0[b] + j * a.dw;
-            const bool ok = mok[b] && ks < a.ksteps && iy >= 0 && iy < a.H && ix >= 0 && ix < a.W && c < a.Cin;
-            const uint32_t off = ok ? (uint32_t)(((int64_t)nb0[b] * a.xs0 + (int64_t)iy * a.xs1 +
-                                                  (int64_t)ix * a.xs2 + xc0 + c) * 2)
-                                    : OOB;
-            xb[b] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0));
-        }
+        for (int st = 0; st < SPS; ++st)
+            issue_step(dst + st * S::STEP);
     };
 
-    f32x4 acc[BLK][NB];
+    // Fragment addresses within a stage. Filter: lane (g, r) reads row
+    // 8g + 4h + r/4 (h = 0, 1), logical chunk 2nb + (r%4)/2, half r%2.
+    // Patch: block b of the wave, pixel 16*(wave*BPW + b) + r, logical chunk g.
+    const int arow = 8 * g + (r >> 2);
+    const int asw = fswz(arow) >> 1;
+    uint32_t abase0[4];
 #pragma unroll
-    for (int b = 0; b < BLK; ++b)
+    for (int nb = 0; nb < NB; ++nb)
+        abase0[nb] = (uint32_t)(S::XSTEP + 128 * arow + 32 * (nb ^ asw) + 16 * ((r & 3) >> 1) + 8 * (r & 1));
+    const uint32_t xbase0 = (uint32_t)(64 * (16 * wave * BPW + r) + 16 * (g ^ ((r >> 2) & 3)));
+    const uint32_t ring_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)ring;
+
+    f32x4 acc[BPW][NB];
+#pragma unroll
+    for (int b = 0; b < BPW; ++b)
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
             acc[b][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const int nchunks = (a.ksteps + KC - 1) / KC;
-    u32x4 fv[FITEMS];
-    chunk_load(0, fv);
-    bf16x8 xb[BLK], xn[BLK];
-    b_load(0, xn);
-    chunk_store(0, fv);
-    __syncthreads();
-
-    for (int q = 0; q < nchunks; ++q) {
-        if (q + 1 < nchunks)
-            chunk_load(q + 1, fv);
-        const uint16_t *ft = fbuf[q & 1];
+    issue_stage(0);
+    issue_stage(1);
+    for (int t = 0; t < a.nstages; ++t) {
+        // Stage t landed for this wave (issued after it: stage t + 1), then
+        // for every wave; stage t - 1's slot is no longer read.
+        wait_vmcnt<S::LOADS>();
+        lds_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        issue_stage(t + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        const uint32_t sb = ring_lds + (uint32_t)((t % NSTAGE) * S::STAGE);
+        uint32_t ab[4];
 #pragma unroll
-        for (int kk = 0; kk < KC; ++kk) {
-            const int ks = q * KC + kk;
-            if (ks < a.ksteps) {
-                // A fragments (see FilterSlice in dense_mfma.hip for the
-                // transpose-read lane layout): lane r of a 16-lane group
-                // addresses row kk*32 + 8g + 4h + r/4, columns 4*(r%4).
-                bf16x8 wf[NB];
+        for (int nb = 0; nb < NB; ++nb)
+            ab[nb] = sb + abase0[nb];
+        i16x4 fa[2][4][2];
+        u32x4 xv[2][BPW];
+        stage_reads<BPW>(ab, sb + xbase0, fa, xv);
 #pragma unroll
-                for (int nb = 0; nb < NB; ++nb) {
-                    i16x4 part[2];
+        for (int st = 0; st < SPS; ++st) {
+            bf16x8 wf[NB];
 #pragma unroll
-                    for (int h = 0; h < 2; ++h)
-                        part[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (__attribute__((address_space(3))) i16x4 *)(ft + (kk * 32 + g * 8 + h * 4 + (r >> 2)) * FP +
-                                                                         nb * 16 + 4 * (r & 3)));
-                    const i16x8 both = {part[0][0], part[0][1], part[0][2], part[0][3],
-                                        part[1][0], part[1][1], part[1][2], part[1][3]};
-                    wf[nb] = __builtin_bit_cast(bf16x8, both);
-                }
-#pragma unroll
-                for (int b = 0; b < BLK; ++b)
-                    xb[b] = xn[b];
-                b_load(ks + 1, xn);
-#pragma unroll
-                for (int b = 0; b < BLK; ++b)
-#pragma unroll
-                    for (int nb = 0; nb < NB; ++nb)
-                        acc[b][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[nb], xb[b], acc[b][nb], 0, 0, 0);
+            for (int nb = 0; nb < NB; ++nb) {
+                const i16x4 lo = fa[st][nb][0], hi = fa[st][nb][1];
+                const i16x8 both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                wf[nb] = __builtin_bit_cast(bf16x8, both);
             }
-        }
-        if (q + 1 < nchunks) {
-            // The other buffer was last read in chunk q - 1, before the
-            // barrier that ended it.
-            chunk_store((q + 1) & 1, fv);
-            __syncthreads();
+#pragma unroll
+            for (int b = 0; b < BPW; ++b)
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+                    acc[b][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[nb], __builtin_bit_cast(bf16x8, xv[st][b]),
+                                                                         acc[b][nb], 0, 0, 0);
         }
     }
+    // The two stages past the end (zeros into free slots) land before the
+    // ring is reused.
+    wait_vmcnt<0>();
+    lds_barrier();
 
-    // Epilogue: lane holds channels o0 + 16nb + 4g + {0..3} of its pixel in
-    // each block.
+    // Epilogue: lane holds channels o0 + 16nb + 4g + {0..3} of pixel
+    // m0 + 16*(wave*BPW + b) + r.
     const __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc(
         a.bias ? (void *)(a.bias + oc0) : (void *)a.F, 0, a.bias ? (int)a.b_records : 0, BUF_WORD3);
     u32x4 bq[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
         bq[nb] = __builtin_amdgcn_raw_buffer_load_b128(br, (uint32_t)((o0 + nb * 16 + g * 4) * 4), 0, 0);
+    const int mw = m0 + 16 * wave * BPW;       // the wave's first pixel
     if constexpr (OUT_BF16) {
-        // Every wave is done with the filter buffer before any overwrites it.
-        __syncthreads();
-        uint8_t *patch = reinterpret_cast<uint8_t *>(&fbuf[0][0]) + wave * 64 * OPITCH;
+        uint8_t *patch = ring + wave * 16 * BPW * OPITCH;
 #pragma unroll
-        for (int b = 0; b < BLK; ++b)
+        for (int b = 0; b < BPW; ++b)
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
                 const f32x4 v = acc[b][nb];
@@ -269,13 +451,13 @@ __global__ __launch_bounds__(GT) void dense_gemm_mfma(GemmArgs a)
             }
         // The patch is this wave's own: its LDS writes complete before its
         // reads (in order), no barrier. Store i: lane L takes pixel
-        // 8i + L/8 of the wave's 64, channels 8*(L%8)..+7.
+        // 8i + L/8 of the wave's, channels 8*(L%8)..+7.
         const int ch = o0 + (lane & 7) * 8;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < 2 * BPW; ++i) {
             const int pp = i * 8 + (lane >> 3);
             const u32x4 w = *reinterpret_cast<const u32x4 *>(patch + pp * OPITCH + (lane & 7) * 16);
-            const int m = mt * GM + wave * 64 + pp;
+            const int m = mw + pp;
             if (m < a.m_total && ch < a.Cout) {
                 const uint32_t ny = fdiv_g((uint32_t)m, a.div_wo);
                 const int x = (int)((uint32_t)m - ny * (uint32_t)a.Wo);
@@ -283,24 +465,70 @@ __global__ __launch_bounds__(GT) void dense_gemm_mfma(GemmArgs a)
                 const int y = (int)(ny - n * (uint32_t)a.Ho);
                 char *yp = static_cast<char *>(a.Y) +
                            ((int64_t)n * a.ys0 + (int64_t)y * a.ys1 + (int64_t)x * a.ys2 + oc0 + ch) * 2;
-                __builtin_nontemporal_store(w, reinterpret_cast<u32x4 *>(yp));   // nt: Conv1D stem -2.5 %
+                __builtin_nontemporal_store(w, reinterpret_cast<u32x4 *>(yp));
             }
         }
     } else {
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-            const int ch = o0 + nb * 16 + g * 4;
+        for (int b = 0; b < BPW; ++b) {
+            const int m = mw + 16 * b + r;
+            if (m >= a.m_total)
+                continue;
+            const uint32_t ny = fdiv_g((uint32_t)m, a.div_wo);
+            const int x = (int)((uint32_t)m - ny * (uint32_t)a.Wo);
+            const uint32_t n = fdiv_g(ny, a.div_ho);
+            const int y = (int)(ny - n * (uint32_t)a.Ho);
 #pragma unroll
-            for (int b = 0; b < BLK; ++b) {
-                if (!mok[b] || ch >= a.Cout)
+            for (int nb = 0; nb < NB; ++nb) {
+                const int ch = o0 + nb * 16 + g * 4;
+                if (ch >= a.Cout)
                     continue;
                 const f32x4 v = acc[b][nb];
                 char *yp = static_cast<char *>(a.Y) +
-                           ((int64_t)nb0[b] * a.ys0 + (int64_t)yo[b] * a.ys1 + (int64_t)xo[b] * a.ys2 + oc0 + ch) * ESZ;
+                           ((int64_t)n * a.ys0 + (int64_t)y * a.ys1 + (int64_t)x * a.ys2 + oc0 + ch) * ESZ;
                 *reinterpret_cast<f32x4 *>(yp) = f32x4{v[0] + __uint_as_float(bq[nb][0]), v[1] + __uint_as_float(bq[nb][1]),
                                                        v[2] + __uint_as_float(bq[nb][2]), v[3] + __uint_as_float(bq[nb][3])};
             }
         }
+    }
+}
+
+// Pixel blocks per wave: the fewest rounds of at most 256 resident tiles
+// (one per compute unit), weighted by the per-tile work BPW.
+int pick_bpw(int64_t m_total, int64_t nt_all)
+{
+    int best = 4;
+    int64_t best_cost = -1;
+    for (int bpw = 2; bpw <= 5; ++bpw) {
+        const int64_t tiles = (m_total + 64 * bpw - 1) / (64 * bpw) * nt_all;
+        const int64_t cost = (tiles + 255) / 256 * bpw;
+        if (best_cost < 0 || cost < best_cost || (cost == best_cost && bpw == 4)) {
+            best = bpw;
+            best_cost = cost;
+        }
+    }
+    return best;
+}
+
+template <int BPW, bool OB>
+hipError_t launch_gemm(const GemmArgs &a, unsigned grid, hipStream_t s)
+{
+    constexpr int lds = GShape<BPW>::LDS;
+    const hipError_t attr = allow_lds<dense_gemm_mfma<BPW, OB>>(lds);
+    if (attr != hipSuccess)
+        return attr;
+    hipLaunchKernelGGL((dense_gemm_mfma<BPW, OB>), dim3(grid), dim3(GT), lds, s, a);
+    return hipGetLastError();
+}
+
+template <bool OB>
+hipError_t launch_gemm_ob(const GemmArgs &a, int bpw, unsigned grid, hipStream_t s)
+{
+    switch (bpw) {
+    case 2: return launch_gemm<2, OB>(a, grid, s);
+    case 3: return launch_gemm<3, OB>(a, grid, s);
+    case 5: return launch_gemm<5, OB>(a, grid, s);
+    default: return launch_gemm<4, OB>(a, grid, s);
     }
 }
 
@@ -329,8 +557,8 @@ bool dense_gemm_bf16_supports(const DenseProblem &p)
     if (x_extent >= (int64_t(1) << 31) || (int64_t)p.KH * p.KW * cin_g * p.Cout * 2 >= (int64_t(1) << 31))
         return false;
     const int64_t m_total = (int64_t)p.N * p.Ho * p.Wo;
-    const int64_t tiles = (m_total + GM - 1) / GM * ((cout_g + GN - 1) / GN) * p.groups;
-    return m_total < (int64_t(1) << 31) - GM && tiles * 8 < (int64_t(1) << 31);
+    const int64_t tiles = (m_total + 127) / 128 * ((cout_g + GN - 1) / GN) * p.groups;   // the smallest tile
+    return m_total < (int64_t(1) << 31) - 320 && tiles * 8 < (int64_t(1) << 31);
 }
 
 hipError_t launch_dense_gemm_bf16(const DenseProblem &p, hipStream_t s)
@@ -352,6 +580,7 @@ hipError_t launch_dense_gemm_bf16(const DenseProblem &p, hipStream_t s)
     a.W = p.W;
     a.Ho = p.Ho;
     a.Wo = p.Wo;
+    a.KH = p.KH;
     a.KW = p.KW;
     a.Cin = p.Cin / p.groups;
     a.Cout = p.Cout / p.groups;
@@ -362,12 +591,13 @@ hipError_t launch_dense_gemm_bf16(const DenseProblem &p, hipStream_t s)
     a.pl = p.pl;
     a.dh = p.dh;
     a.dw = p.dw;
-    a.cs_steps = (a.Cin + 31) / 32;
-    a.ksteps = p.KH * p.KW * a.cs_steps;
+    a.ksteps = p.KH * p.KW * ((a.Cin + 31) / 32);
+    a.nstages = (a.ksteps + SPS - 1) / SPS;
     a.m_total = p.N * p.Ho * p.Wo;
     a.n_tiles = (a.Cout + GN - 1) / GN;
-    const int m_tiles = (a.m_total + GM - 1) / GM;
     a.nt_all = a.n_tiles * p.groups;
+    const int bpw = pick_bpw(a.m_total, a.nt_all);
+    const int m_tiles = (a.m_total + 64 * bpw - 1) / (64 * bpw);
     a.tiles = m_tiles * a.nt_all;
     a.x_records = (uint32_t)(((int64_t)(p.N - 1) * p.xs[0] + (int64_t)(p.H - 1) * p.xs[1] +
                               (int64_t)(p.W - 1) * p.xs[2] + p.Cin) * 2);
@@ -376,11 +606,7 @@ hipError_t launch_dense_gemm_bf16(const DenseProblem &p, hipStream_t s)
     a.div_wo = make_fastdiv_g((uint32_t)p.Wo);
     a.div_ho = make_fastdiv_g((uint32_t)p.Ho);
     const unsigned grid = (unsigned)((a.tiles + 7) / 8 * 8);
-    if (p.ydt == CONV_BF16)
-        hipLaunchKernelGGL(dense_gemm_mfma<true>, dim3(grid), dim3(GT), 0, s, a);
-    else
-        hipLaunchKernelGGL(dense_gemm_mfma<false>, dim3(grid), dim3(GT), 0, s, a);
-    return hipGetLastError();
+    return p.ydt == CONV_BF16 ? launch_gemm_ob<true>(a, bpw, grid, s) : launch_gemm_ob<false>(a, bpw, grid, s);
 }
 
 }  // namespace convfwd
