@@ -14,12 +14,18 @@
 // holds nothing per band: the GEMM's M axis is the flat output pixel index
 // m = (n*Ho + y)*Wo + x, so any output shape tiles evenly.
 //
-// Work decomposition (one workgroup = 4 waves = 256 threads):
-//  * A tile is 64*BPW output pixels x 64 output channels of one group. Wave
-//    w owns the tile's 16-pixel blocks w*BPW .. w*BPW + BPW - 1 and all 64
-//    channels (four 16-channel column blocks): 4*BPW accumulators. BPW (2 to
-//    5) is chosen per launch so the tiles fill the compute units in as few
-//    rounds as possible.
+// Work decomposition (one workgroup = 8 waves = 512 threads, two per SIMD):
+//  * A tile is 64*BPW output pixels x 64 output channels of one group.
+//  * Four waves only load: each issues its share of every stage's loads,
+//    waits for them and meets the others at the stage's barrier. Issuing a
+//    stage's gathered patch loads holds a wave for about as long as the
+//    stage's MFMAs take (the address unit takes ~37 clocks per 16-pixel
+//    gather), so a wave that both loads and computes leaves the matrix pipe
+//    idle that long.
+//  * Four waves only compute: computing wave w owns the tile's 16-pixel
+//    blocks w*BPW .. w*BPW + BPW - 1 and all 64 channels (four 16-channel
+//    column blocks): 4*BPW accumulators. BPW (2 to 5) is chosen per launch
+//    so the tiles fill the compute units in as few rounds as possible.
 //  * The K axis runs over steps (32-channel slice, tap i, tap j): the taps
 //    of one slice follow each other, so they read input lines still in the
 //    caches (the sum is the same; only the fp32 rounding order differs from
@@ -57,7 +63,8 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 
-constexpr int GT = 256;                 // threads per workgroup
+constexpr int LOADERS = 4;              // waves that only issue loads
+constexpr int GT = 512;                 // threads per workgroup: 4 loading and 4 computing waves
 constexpr int GN = 64;                  // output channels per tile
 constexpr int NB = 4;                   // 16-channel column blocks per wave
 constexpr int SPS = 2;                  // steps per stage
@@ -296,88 +303,115 @@ __global__ __launch_bounds__(GT) void dense_gemm_mfma(GemmArgs a)
     const int xc0 = grp * a.Cin, oc0 = grp * a.Cout;
     const int m0 = mt * S::M;
 
-    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t *>(a.X), 0, (int)a.x_records, BUF_WORD3);
-    const __amdgpu_buffer_rsrc_t fr = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t *>(a.F), 0, (int)a.f_records, BUF_WORD3);
-
-    // Patch loads: load v of wave w fills tile pixels 16*(4v + w) ..+15,
-    // lane L taking pixel 16*(4v + w) + L/4 and stored chunk L % 4, which
-    // holds logical chunk (L % 4) ^ ((pixel / 4) % 4) (8 channels).
-    const int xchunk = (lane & 3) ^ ((lane >> 4) & 3);
-    int xb0[BPW], iy0[BPW], ix0[BPW];
-    bool mok[BPW];
-#pragma unroll
-    for (int v = 0; v < BPW; ++v) {
-        const int m = m0 + 16 * (4 * v + wave) + (lane >> 2);
-        mok[v] = m < a.m_total;
-        const uint32_t mm = mok[v] ? (uint32_t)m : 0u;
-        const uint32_t ny = fdiv_g(mm, a.div_wo);
-        const int x = (int)(mm - ny * (uint32_t)a.Wo);
-        const uint32_t n = fdiv_g(ny, a.div_ho);
-        const int y = (int)(ny - n * (uint32_t)a.Ho);
-        xb0[v] = (int)(n * (uint32_t)a.xs0) + xc0 + 8 * xchunk;
-        iy0[v] = y * a.sh - a.pt;
-        ix0[v] = x * a.sw - a.pl;
-    }
-    // Filter loads: wave w fills rows 8w .. 8w+7 of a step's slice, lane L
-    // row 8w + L/8, stored chunk L % 8 (logical chunk (L % 8) ^ fswz(row)).
-    const int frow = 8 * wave + (lane >> 3);
-    const int fcol = o0 + 8 * ((lane & 7) ^ fswz(frow));
-    const bool fcol_ok = fcol < a.Cout;
-
-    // The step whose loads go out next: tap (li, lj), channel slice lcs.
-    int lks = 0, lcs = 0, li = 0, lj = 0;
-    auto issue_step = [&](uint8_t *dst) __attribute__((always_inline)) {
-        const bool kok = lks < a.ksteps;
-        const int c = lcs * 32;
+    if (wave < LOADERS) {
+        // ---- Loader wave p: issues its share of every stage's loads and
+        // waits for them; the barrier then publishes the stage.
+        const int pw = wave;
+        const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t *>(a.X), 0, (int)a.x_records, BUF_WORD3);
+        const __amdgpu_buffer_rsrc_t fr = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t *>(a.F), 0, (int)a.f_records, BUF_WORD3);
+        // Patch loads: load v of loader p fills tile pixels 16*(4v + p) ..+15,
+        // lane L taking pixel 16*(4v + p) + L/4 and stored chunk L % 4, which
+        // holds logical chunk (L % 4) ^ ((pixel / 4) % 4) (8 channels).
+        const int xchunk = (lane & 3) ^ ((lane >> 4) & 3);
+        int xb0[BPW], iy0[BPW], ix0[BPW];
+        bool mok[BPW];
 #pragma unroll
         for (int v = 0; v < BPW; ++v) {
-            const int iy = iy0[v] + li * a.dh;
-            const int ix = ix0[v] + lj * a.dw;
-            const bool ok = kok && mok[v] && (unsigned)iy < (unsigned)a.H && (unsigned)ix < (unsigned)a.W &&
-                            c + 8 * xchunk < a.Cin;
-            const uint32_t off =
-                ok ? ((uint32_t)xb0[v] + (uint32_t)iy * (uint32_t)a.xs1 + (uint32_t)ix * (uint32_t)a.xs2 + (uint32_t)c) * 2u
-                   : OOB;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                xr, (__attribute__((address_space(3))) void *)(dst + 1024 * (4 * v + wave)), 16, off, 0, 0, 0);
+            const int m = m0 + 16 * (4 * v + pw) + (lane >> 2);
+            mok[v] = m < a.m_total;
+            const uint32_t mm = mok[v] ? (uint32_t)m : 0u;
+            const uint32_t ny = fdiv_g(mm, a.div_wo);
+            const int x = (int)(mm - ny * (uint32_t)a.Wo);
+            const uint32_t n = fdiv_g(ny, a.div_ho);
+            const int y = (int)(ny - n * (uint32_t)a.Ho);
+            xb0[v] = (int)(n * (uint32_t)a.xs0) + xc0 + 8 * xchunk;
+            iy0[v] = y * a.sh - a.pt;
+            ix0[v] = x * a.sw - a.pl;
         }
-        {
-            const int tap = li * a.KW + lj;
-            const bool ok = kok && fcol_ok && c + frow < a.Cin;
-            const uint32_t off = ok ? (uint32_t)((((int64_t)tap * a.Cin + c + frow) * a.f_ld + oc0 + fcol) * 2) : OOB;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                fr, (__attribute__((address_space(3))) void *)(dst + S::XSTEP + 1024 * wave), 16, off, 0, 0, 0);
-        }
-        // Next step: tap column, then tap row, then channel slice (the taps
-        // of one slice read neighbouring input lines while they are cached).
-        ++lks;
-        if (++lj == a.KW) {
-            lj = 0;
-            if (++li == a.KH) {
-                li = 0;
-                ++lcs;
-            }
-        }
-    };
-    auto issue_stage = [&](int t) __attribute__((always_inline)) {
-        uint8_t *dst = ring + (t % NSTAGE) * S::STAGE;
-#pragma unroll
-        for (int st = 0; st < SPS; ++st)
-            issue_step(dst + st * S::STEP);
-    };
+        // Filter loads: loader p fills rows 8p .. 8p+7 of a step's slice,
+        // lane L row 8p + L/8, stored chunk L % 8 (logical chunk
+        // (L % 8) ^ fswz(row)).
+        const int frow = 8 * pw + (lane >> 3);
+        const int fcol = o0 + 8 * ((lane & 7) ^ fswz(frow));
+        const bool fcol_ok = fcol < a.Cout;
 
+        // The step whose loads go out next: tap (li, lj), channel slice lcs.
+        int lks = 0, lcs = 0, li = 0, lj = 0;
+        auto issue_step = [&](uint8_t *dst) __attribute__((always_inline)) {
+            const bool kok = lks < a.ksteps;
+            const int c = lcs * 32;
+#pragma unroll
+            for (int v = 0; v < BPW; ++v) {
+                const int iy = iy0[v] + li * a.dh;
+                const int ix = ix0[v] + lj * a.dw;
+                const bool ok = kok && mok[v] && (unsigned)iy < (unsigned)a.H && (unsigned)ix < (unsigned)a.W &&
+                                c + 8 * xchunk < a.Cin;
+                const uint32_t off =
+                    ok ? ((uint32_t)xb0[v] + (uint32_t)iy * (uint32_t)a.xs1 + (uint32_t)ix * (uint32_t)a.xs2 + (uint32_t)c) * 2u
+                       : OOB;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    xr, (__attribute__((address_space(3))) void *)(dst + 1024 * (4 * v + pw)), 16, off, 0, 0, 0);
+            }
+            {
+                const int tap = li * a.KW + lj;
+                const bool ok = kok && fcol_ok && c + frow < a.Cin;
+                const uint32_t off = ok ? (uint32_t)((((int64_t)tap * a.Cin + c + frow) * a.f_ld + oc0 + fcol) * 2) : OOB;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    fr, (__attribute__((address_space(3))) void *)(dst + S::XSTEP + 1024 * pw), 16, off, 0, 0, 0);
+            }
+            // Next step: tap column, then tap row, then channel slice (the
+            // taps of one slice read neighbouring input lines while they are
+            // cached).
+            ++lks;
+            if (++lj == a.KW) {
+                lj = 0;
+                if (++li == a.KH) {
+                    li = 0;
+                    ++lcs;
+                }
+            }
+        };
+        auto issue_stage = [&](int t) __attribute__((always_inline)) {
+            uint8_t *dst = ring + (t % NSTAGE) * S::STAGE;
+#pragma unroll
+            for (int st = 0; st < SPS; ++st)
+                issue_step(dst + st * S::STEP);
+        };
+
+        issue_stage(0);
+        issue_stage(1);
+        for (int t = 0; t < a.nstages; ++t) {
+            // Stage t landed for this loader (issued after it: stage t + 1);
+            // at the barrier, for every loader. Past the barrier the
+            // computing waves have read stage t - 1: its slot takes stage
+            // t + 2.
+            wait_vmcnt<S::LOADS>();
+            lds_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+            issue_stage(t + 2);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // The stages past the end (zeros into free slots) land before the
+        // ring is reused for the output.
+        wait_vmcnt<0>();
+        lds_barrier();
+        return;
+    }
+
+    // ---- Computing wave w: MFMAs on the stage published by the barrier.
+    const int cw = wave - LOADERS;
     // Fragment addresses within a stage. Filter: lane (g, r) reads row
     // 8g + 4h + r/4 (h = 0, 1), logical chunk 2nb + (r%4)/2, half r%2.
-    // Patch: block b of the wave, pixel 16*(wave*BPW + b) + r, logical chunk g.
+    // Patch: block b of the wave, pixel 16*(cw*BPW + b) + r, logical chunk g.
     const int arow = 8 * g + (r >> 2);
     const int asw = fswz(arow) >> 1;
     uint32_t abase0[4];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
         abase0[nb] = (uint32_t)(S::XSTEP + 128 * arow + 32 * (nb ^ asw) + 16 * ((r & 3) >> 1) + 8 * (r & 1));
-    const uint32_t xbase0 = (uint32_t)(64 * (16 * wave * BPW + r) + 16 * (g ^ ((r >> 2) & 3)));
+    const uint32_t xbase0 = (uint32_t)(64 * (16 * cw * BPW + r) + 16 * (g ^ ((r >> 2) & 3)));
     const uint32_t ring_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)ring;
 
     f32x4 acc[BPW][NB];
@@ -387,15 +421,9 @@ __global__ __launch_bounds__(GT) void dense_gemm_mfma(GemmArgs a)
         for (int nb = 0; nb < NB; ++nb)
             acc[b][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    issue_stage(0);
-    issue_stage(1);
     for (int t = 0; t < a.nstages; ++t) {
-        // Stage t landed for this wave (issued after it: stage t + 1), then
-        // for every wave; stage t - 1's slot is no longer read.
-        wait_vmcnt<S::LOADS>();
+        // Stage t is in LDS for every loader; stage t - 1's reads are done.
         lds_barrier();
-        __builtin_amdgcn_sched_barrier(0);
-        issue_stage(t + 2);
         __builtin_amdgcn_sched_barrier(0);
         const uint32_t sb = ring_lds + (uint32_t)((t % NSTAGE) * S::STAGE);
         uint32_t ab[4];
@@ -422,22 +450,20 @@ __global__ __launch_bounds__(GT) void dense_gemm_mfma(GemmArgs a)
                                                                          acc[b][nb], 0, 0, 0);
         }
     }
-    // The two stages past the end (zeros into free slots) land before the
-    // ring is reused.
-    wait_vmcnt<0>();
+    // Every loader's stages past the end have landed: the ring is free.
     lds_barrier();
 
     // Epilogue: lane holds channels o0 + 16nb + 4g + {0..3} of pixel
-    // m0 + 16*(wave*BPW + b) + r.
+    // m0 + 16*(cw*BPW + b) + r.
     const __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc(
         a.bias ? (void *)(a.bias + oc0) : (void *)a.F, 0, a.bias ? (int)a.b_records : 0, BUF_WORD3);
     u32x4 bq[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
         bq[nb] = __builtin_amdgcn_raw_buffer_load_b128(br, (uint32_t)((o0 + nb * 16 + g * 4) * 4), 0, 0);
-    const int mw = m0 + 16 * wave * BPW;       // the wave's first pixel
+    const int mw = m0 + 16 * cw * BPW;       // the wave's first pixel
     if constexpr (OUT_BF16) {
-        uint8_t *patch = ring + wave * 16 * BPW * OPITCH;
+        uint8_t *patch = ring + cw * 16 * BPW * OPITCH;
 #pragma unroll
         for (int b = 0; b < BPW; ++b)
 #pragma unroll
