@@ -210,6 +210,14 @@ hipError_t launch_dense_tiled(const DenseProblem &p, hipStream_t s)
     if (p.xdt != CONV_BF16)
         return plain_window(p) && dense_mfma_f32_supports(p) ? launch_dense_mfma_f32(p, s)
                                                               : launch_dense_gemm_f32(p, s);
+    // Strided windows whose groups fill 64-channel tiles: the GEMM kernel
+    // (3x3 stride 2 -> 128 channels: 10.9 us against 16.9 on the row
+    // kernel). Narrower groups stay with the row kernel's block-diagonal
+    // packing.
+    const bool strided = p.sh > 1 || p.sw > 1;
+    const bool wide_groups = p.groups == 1 || (p.Cout / p.groups) % 64 == 0;
+    if (strided && wide_groups && dense_gemm_bf16_supports(p))
+        return launch_dense_gemm_bf16(p, s);
     if (dense_mfma_bf16_supports(p))
         return launch_dense_mfma_bf16(p, s);
     return launch_dense_gemm_bf16(p, s);

@@ -8,37 +8,43 @@
 // row y*sh + i*dh - pt and column x*sw + j*dw - pl, zero outside) and its
 // groups (section "Find the same sum in CKE's C kernels").
 //
-// This kernel takes what the row kernel (dense_mfma.hip) declines: more
-// than 64 input channels under a 3x3 window, 5x5 and larger windows,
-// dilation, unequal strides, and 1D sequences longer than a row tile. It
-// holds nothing per band: the GEMM's M axis is the flat output pixel index
+// This kernel takes strided windows whose groups fill its 64-channel tiles,
+// and what the row kernel (dense_mfma.hip) declines: more than 64 input
+// channels under a 3x3 window, 5x5 and larger windows, dilation, unequal
+// strides, and 1D sequences longer than a row tile. It holds nothing per
+// band: the GEMM's M axis is the flat output pixel index
 // m = (n*Ho + y)*Wo + x, so any output shape tiles evenly.
 //
-// Work decomposition (one workgroup = 8 waves = 512 threads, two per SIMD):
+// Work decomposition (one workgroup = 12 waves = 768 threads, three per
+// SIMD):
 //  * A tile is 64*BPW output pixels x 64 output channels of one group.
-//  * Four waves only load: each issues its share of every stage's loads,
+//  * Eight waves only load: each issues its share of every stage's loads,
 //    waits for them and meets the others at the stage's barrier. Issuing a
-//    stage's gathered patch loads holds a wave for about as long as the
-//    stage's MFMAs take (the address unit takes ~37 clocks per 16-pixel
-//    gather), so a wave that both loads and computes leaves the matrix pipe
-//    idle that long.
+//    stage's loads holds a wave for about as long as the stage's MFMAs take
+//    (timestamps: 0.9 us a stage with four issuing waves, whether each load
+//    gathers 16 pixels x 64 bytes or 8 pixels x 128 bytes), so a wave that
+//    both loads and computes leaves the matrix pipe idle that long, and
+//    more issuing waves shorten it.
 //  * Four waves only compute: computing wave w owns the tile's 16-pixel
 //    blocks w*BPW .. w*BPW + BPW - 1 and all 64 channels (four 16-channel
 //    column blocks): 4*BPW accumulators. BPW (2 to 5) is chosen per launch
 //    so the tiles fill the compute units in as few rounds as possible.
-//  * The K axis runs over steps (32-channel slice, tap i, tap j): the taps
+//  * The K axis runs over stages (64-channel slice, tap i, tap j): the taps
 //    of one slice follow each other, so they read input lines still in the
 //    caches (the sum is the same; only the fp32 rounding order differs from
-//    the lecture's (i, j, c)). Each step's operands are staged in LDS: the
-//    patch slice (the tile's pixels x 32 channels, 64 bytes a pixel) and the
-//    filter slice F[i, j, c:c+32, o0:o0+64] (4 KB), both with loads that
-//    write LDS directly (each wave instruction fills 1 KB contiguously; taps
-//    in the padding, pixels past the end and channels past Cin load zeros).
-//  * Steps go two to a stage through a ring of three stages: stage t + 2 is
-//    requested as stage t starts, so two stages are in flight while one is
-//    used. The waits are explicit counts: every memory instruction in the
-//    loop is unconditional (steps past the end load zeros into a free slot),
-//    so the number issued after stage t is a constant.
+//    the lecture's (i, j, c)). A stage is two MFMA k-steps of 32 channels.
+//    Its operands are staged in LDS: the patch slice (the tile's pixels x 64
+//    channels, one whole 128-byte line a pixel: the address unit's time goes
+//    by lines touched, so 8 pixels x 128 bytes per load cost about half of
+//    16 pixels x 64 bytes) and the filter slice F[i, j, c:c+64, o0:o0+64]
+//    (8 KB), both with loads that write LDS directly (each wave instruction
+//    fills 1 KB contiguously; taps in the padding, pixels past the end and
+//    channels past Cin load zeros).
+//  * Stages go through a ring of three: stage t + 2 is requested as stage t
+//    starts, so two stages are in flight while one is used. The waits are
+//    explicit counts: every memory instruction in the loop is unconditional
+//    (stages past the end load zeros into a free slot), so the number issued
+//    after stage t is a constant.
 //  * Filter fragments are read with the gfx950 transpose read, patch
 //    fragments with 16-byte reads; both are placed with an XOR swizzle so the
 //    16 lanes of a read hit distinct banks. All of a stage's fragment reads
@@ -63,13 +69,12 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 
-constexpr int LOADERS = 4;              // waves that only issue loads
-constexpr int GT = 512;                 // threads per workgroup: 4 loading and 4 computing waves
+constexpr int LOADERS = 8;              // waves that only issue loads
+constexpr int GT = 64 * (LOADERS + 4);  // threads per workgroup: the loading and 4 computing waves
 constexpr int GN = 64;                  // output channels per tile
 constexpr int NB = 4;                   // 16-channel column blocks per wave
-constexpr int SPS = 2;                  // steps per stage
 constexpr int NSTAGE = 3;               // stages in the LDS ring
-constexpr int FSTEP = 32 * GN * 2;      // filter bytes per step
+constexpr int FSTAGE = 64 * GN * 2;     // filter bytes per stage (64 rows of 128 bytes)
 constexpr int OPITCH = GN * 2 + 16;     // LDS pitch of one pixel of a wave's bf16 output patch (bytes)
 constexpr uint32_t OOB = 0x80000000u;
 constexpr int BUF_WORD3 = 0x00020000;
@@ -78,13 +83,15 @@ constexpr int LDS_MAX = 160 * 1024;
 template <int BPW>
 struct GShape {
     static constexpr int M = 64 * BPW;                  // pixels per tile
-    static constexpr int XSTEP = M * 64;                // patch bytes per step
-    static constexpr int STEP = XSTEP + FSTEP;
-    static constexpr int STAGE = SPS * STEP;
+    static constexpr int XSTAGE = M * 128;              // patch bytes per stage
+    static constexpr int STAGE = XSTAGE + FSTAGE;
     static constexpr int LDS = NSTAGE * STAGE;
-    static constexpr int LOADS = SPS * (BPW + 1);       // loads per thread per stage
+    static constexpr int XLOADS = XSTAGE / (LOADERS * 64 * 16);   // patch loads per loading lane: 2 * BPW
+    static constexpr int FLOADS = FSTAGE / (LOADERS * 64 * 16);   // filter loads per loading lane: 1
+    static constexpr int LOADS = XLOADS + FLOADS;       // loads per loading lane per stage
     static_assert(LDS <= LDS_MAX, "LDS");
     static_assert(4 * 16 * BPW * OPITCH <= LDS, "output patches fit in the ring");
+    static_assert(XLOADS * LOADERS * 64 * 16 == XSTAGE && FLOADS * LOADERS * 64 * 16 == FSTAGE, "whole loads");
     static_assert(LOADS < 64, "vmcnt holds 6 bits");
 };
 
@@ -113,23 +120,23 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 
 // Physical 16-byte chunk of logical chunk c in row k of a staged filter
 // slice (rows of 128 bytes): the 8 rows that one half-wave's transpose read
-// touches fall in 8 distinct pairs of bank groups. (Patch pixels P, 64
-// bytes, keep logical chunk c at c ^ ((P >> 2) & 3): the 16 pixels of a
+// touches fall in 8 distinct pairs of bank groups. (Patch pixels P, also
+// 128 bytes, keep logical chunk c at c ^ ((P >> 1) & 7): the 16 pixels of a
 // fragment read fall in 16 distinct bank groups.)
 __host__ __device__ constexpr int fswz(int k) { return (((k >> 1) & 1) << 1) | (((k >> 3) & 1) << 2); }
 
-// Every fragment read of one stage (two steps): for each step the four
-// filter fragments (two transposed 8-byte reads each, at +0 and +512 bytes
-// from the column block's base) and the BPW patch fragments (16-byte reads
-// 1 KB apart); step 1 sits STEP bytes after step 0. Outputs are
+// Every fragment read of one stage: for each k-step s the four filter
+// fragments (two transposed 8-byte reads each, at +0 and +512 bytes from the
+// column block's base, k-step 1 another 4 KB on) and the BPW patch
+// fragments (16-byte reads 2 KB apart from k-step s's base). Outputs are
 // early-clobber so no read lands in an address register still to be used.
 template <int BPW>
-__device__ __forceinline__ void stage_reads(const uint32_t (&abase)[4], uint32_t xbase, i16x4 (&a)[2][4][2],
-                                            u32x4 (&b)[2][BPW]);
+__device__ __forceinline__ void stage_reads(const uint32_t (&abase)[4], const uint32_t (&xbase)[2],
+                                            i16x4 (&a)[2][4][2], u32x4 (&b)[2][BPW]);
 
 template <>
-__device__ __forceinline__ void stage_reads<2>(const uint32_t (&abase)[4], uint32_t xbase, i16x4 (&a)[2][4][2],
-                                                 u32x4 (&b)[2][2])
+__device__ __forceinline__ void stage_reads<2>(const uint32_t (&abase)[4], const uint32_t (&xbase)[2],
+                                                 i16x4 (&a)[2][4][2], u32x4 (&b)[2][2])
 {
     asm volatile("ds_read_b64_tr_b16 %0, %20 offset:0\n\t"
                  "ds_read_b64_tr_b16 %1, %20 offset:512\n\t"
@@ -140,26 +147,26 @@ __device__ __forceinline__ void stage_reads<2>(const uint32_t (&abase)[4], uint3
                  "ds_read_b64_tr_b16 %6, %23 offset:0\n\t"
                  "ds_read_b64_tr_b16 %7, %23 offset:512\n\t"
                  "ds_read_b128 %16, %24 offset:0\n\t"
-                 "ds_read_b128 %17, %24 offset:1024\n\t"
-                 "ds_read_b64_tr_b16 %8, %20 offset:12288\n\t"
-                 "ds_read_b64_tr_b16 %9, %20 offset:12800\n\t"
-                 "ds_read_b64_tr_b16 %10, %21 offset:12288\n\t"
-                 "ds_read_b64_tr_b16 %11, %21 offset:12800\n\t"
-                 "ds_read_b64_tr_b16 %12, %22 offset:12288\n\t"
-                 "ds_read_b64_tr_b16 %13, %22 offset:12800\n\t"
-                 "ds_read_b64_tr_b16 %14, %23 offset:12288\n\t"
-                 "ds_read_b64_tr_b16 %15, %23 offset:12800\n\t"
-                 "ds_read_b128 %18, %24 offset:12288\n\t"
-                 "ds_read_b128 %19, %24 offset:13312\n\t"
+                 "ds_read_b128 %17, %24 offset:2048\n\t"
+                 "ds_read_b64_tr_b16 %8, %20 offset:4096\n\t"
+                 "ds_read_b64_tr_b16 %9, %20 offset:4608\n\t"
+                 "ds_read_b64_tr_b16 %10, %21 offset:4096\n\t"
+                 "ds_read_b64_tr_b16 %11, %21 offset:4608\n\t"
+                 "ds_read_b64_tr_b16 %12, %22 offset:4096\n\t"
+                 "ds_read_b64_tr_b16 %13, %22 offset:4608\n\t"
+                 "ds_read_b64_tr_b16 %14, %23 offset:4096\n\t"
+                 "ds_read_b64_tr_b16 %15, %23 offset:4608\n\t"
+                 "ds_read_b128 %18, %25 offset:0\n\t"
+                 "ds_read_b128 %19, %25 offset:2048\n\t"
                  "s_waitcnt lgkmcnt(0)"
                  : "=&v"(a[0][0][0]), "=&v"(a[0][0][1]), "=&v"(a[0][1][0]), "=&v"(a[0][1][1]), "=&v"(a[0][2][0]), "=&v"(a[0][2][1]), "=&v"(a[0][3][0]), "=&v"(a[0][3][1]), "=&v"(a[1][0][0]), "=&v"(a[1][0][1]), "=&v"(a[1][1][0]), "=&v"(a[1][1][1]), "=&v"(a[1][2][0]), "=&v"(a[1][2][1]), "=&v"(a[1][3][0]), "=&v"(a[1][3][1]), "=&v"(b[0][0]), "=&v"(b[0][1]), "=&v"(b[1][0]), "=&v"(b[1][1])
-                 : "v"(abase[0]), "v"(abase[1]), "v"(abase[2]), "v"(abase[3]), "v"(xbase)
+                 : "v"(abase[0]), "v"(abase[1]), "v"(abase[2]), "v"(abase[3]), "v"(xbase[0]), "v"(xbase[1])
                  : "memory");
 }
 
 template <>
-__device__ __forceinline__ void stage_reads<3>(const uint32_t (&abase)[4], uint32_t xbase, i16x4 (&a)[2][4][2],
-                                                 u32x4 (&b)[2][3])
+__device__ __forceinline__ void stage_reads<3>(const uint32_t (&abase)[4], const uint32_t (&xbase)[2],
+                                                 i16x4 (&a)[2][4][2], u32x4 (&b)[2][3])
 {
     asm volatile("ds_read_b64_tr_b16 %0, %22 offset:0\n\t"
                  "ds_read_b64_tr_b16 %1, %22 offset:512\n\t"
@@ -170,28 +177,28 @@ __device__ __forceinline__ void stage_reads<3>(const uint32_t (&abase)[4], uint3
                  "ds_read_b64_tr_b16 %6, %25 offset:0\n\t"
                  "ds_read_b64_tr_b16 %7, %25 offset:512\n\t"
                  "ds_read_b128 %16, %26 offset:0\n\t"
-                 "ds_read_b128 %17, %26 offset:1024\n\t"
-                 "ds_read_b128 %18, %26 offset:2048\n\t"
-                 "ds_read_b64_tr_b16 %8, %22 offset:16384\n\t"
-                 "ds_read_b64_tr_b16 %9, %22 offset:16896\n\t"
-                 "ds_read_b64_tr_b16 %10, %23 offset:16384\n\t"
-                 "ds_read_b64_tr_b16 %11, %23 offset:16896\n\t"
-                 "ds_read_b64_tr_b16 %12, %24 offset:16384\n\t"
-                 "ds_read_b64_tr_b16 %13, %24 offset:16896\n\t"
-                 "ds_read_b64_tr_b16 %14, %25 offset:16384\n\t"
-                 "ds_read_b64_tr_b16 %15, %25 offset:16896\n\t"
-                 "ds_read_b128 %19, %26 offset:16384\n\t"
-                 "ds_read_b128 %20, %26 offset:17408\n\t"
-                 "ds_read_b128 %21, %26 offset:18432\n\t"
+                 "ds_read_b128 %17, %26 offset:2048\n\t"
+                 "ds_read_b128 %18, %26 offset:4096\n\t"
+                 "ds_read_b64_tr_b16 %8, %22 offset:4096\n\t"
+                 "ds_read_b64_tr_b16 %9, %22 offset:4608\n\t"
+                 "ds_read_b64_tr_b16 %10, %23 offset:4096\n\t"
+                 "ds_read_b64_tr_b16 %11, %23 offset:4608\n\t"
+                 "ds_read_b64_tr_b16 %12, %24 offset:4096\n\t"
+                 "ds_read_b64_tr_b16 %13, %24 offset:4608\n\t"
+                 "ds_read_b64_tr_b16 %14, %25 offset:4096\n\t"
+                 "ds_read_b64_tr_b16 %15, %25 offset:4608\n\t"
+                 "ds_read_b128 %19, %27 offset:0\n\t"
+                 "ds_read_b128 %20, %27 offset:2048\n\t"
+                 "ds_read_b128 %21, %27 offset:4096\n\t"
                  "s_waitcnt lgkmcnt(0)"
                  : "=&v"(a[0][0][0]), "=&v"(a[0][0][1]), "=&v"(a[0][1][0]), "=&v"(a[0][1][1]), "=&v"(a[0][2][0]), "=&v"(a[0][2][1]), "=&v"(a[0][3][0]), "=&v"(a[0][3][1]), "=&v"(a[1][0][0]), "=&v"(a[1][0][1]), "=&v"(a[1][1][0]), "=&v"(a[1][1][1]), "=&v"(a[1][2][0]), "=&v"(a[1][2][1]), "=&v"(a[1][3][0]), "=&v"(a[1][3][1]), "=&v"(b[0][0]), "=&v"(b[0][1]), "=&v"(b[0][2]), "=&v"(b[1][0]), "=&v"(b[1][1]), "=&v"(b[1][2])
-                 : "v"(abase[0]), "v"(abase[1]), "v"(abase[2]), "v"(abase[3]), "v"(xbase)
+                 : "v"(abase[0]), "v"(abase[1]), "v"(abase[2]), "v"(abase[3]), "v"(xbase[0]), "v"(xbase[1])
                  : "memory");
 }
 
 template <>
-__device__ __forceinline__ void stage_reads<4>(const uint32_t (&abase)[4], uint32_t xbase, i16x4 (&a)[2][4][2],
-                                                 u32x4 (&b)[2][4])
+__device__ __forceinline__ void stage_reads<4>(const uint32_t (&abase)[4], const uint32_t (&xbase)[2],
+                                                 i16x4 (&a)[2][4][2], u32x4 (&b)[2][4])
 {
     asm volatile("ds_read_b64_tr_b16 %0, %24 offset:0\n\t"
                  "ds_read_b64_tr_b16 %1, %24 offset:512\n\t"
@@ -202,30 +209,30 @@ __device__ __forceinline__ void stage_reads<4>(const uint32_t (&abase)[4], uint3
                  "ds_read_b64_tr_b16 %6, %27 offset:0\n\t"
                  "ds_read_b64_tr_b16 %7, %27 offset:512\n\t"
                  "ds_read_b128 %16, %28 offset:0\n\t"
-                 "ds_read_b128 %17, %28 offset:1024\n\t"
-                 "ds_read_b128 %18, %28 offset:2048\n\t"
-                 "ds_read_b128 %19, %28 offset:3072\n\t"
-                 "ds_read_b64_tr_b16 %8, %24 offset:20480\n\t"
-                 "ds_read_b64_tr_b16 %9, %24 offset:20992\n\t"
-                 "ds_read_b64_tr_b16 %10, %25 offset:20480\n\t"
-                 "ds_read_b64_tr_b16 %11, %25 offset:20992\n\t"
-                 "ds_read_b64_tr_b16 %12, %26 offset:20480\n\t"
-                 "ds_read_b64_tr_b16 %13, %26 offset:20992\n\t"
-                 "ds_read_b64_tr_b16 %14, %27 offset:20480\n\t"
-                 "ds_read_b64_tr_b16 %15, %27 offset:20992\n\t"
-                 "ds_read_b128 %20, %28 offset:20480\n\t"
-                 "ds_read_b128 %21, %28 offset:21504\n\t"
-                 "ds_read_b128 %22, %28 offset:22528\n\t"
-                 "ds_read_b128 %23, %28 offset:23552\n\t"
+                 "ds_read_b128 %17, %28 offset:2048\n\t"
+                 "ds_read_b128 %18, %28 offset:4096\n\t"
+                 "ds_read_b128 %19, %28 offset:6144\n\t"
+                 "ds_read_b64_tr_b16 %8, %24 offset:4096\n\t"
+                 "ds_read_b64_tr_b16 %9, %24 offset:4608\n\t"
+                 "ds_read_b64_tr_b16 %10, %25 offset:4096\n\t"
+                 "ds_read_b64_tr_b16 %11, %25 offset:4608\n\t"
+                 "ds_read_b64_tr_b16 %12, %26 offset:4096\n\t"
+                 "ds_read_b64_tr_b16 %13, %26 offset:4608\n\t"
+                 "ds_read_b64_tr_b16 %14, %27 offset:4096\n\t"
+                 "ds_read_b64_tr_b16 %15, %27 offset:4608\n\t"
+                 "ds_read_b128 %20, %29 offset:0\n\t"
+                 "ds_read_b128 %21, %29 offset:2048\n\t"
+                 "ds_read_b128 %22, %29 offset:4096\n\t"
+                 "ds_read_b128 %23, %29 offset:6144\n\t"
                  "s_waitcnt lgkmcnt(0)"
                  : "=&v"(a[0][0][0]), "=&v"(a[0][0][1]), "=&v"(a[0][1][0]), "=&v"(a[0][1][1]), "=&v"(a[0][2][0]), "=&v"(a[0][2][1]), "=&v"(a[0][3][0]), "=&v"(a[0][3][1]), "=&v"(a[1][0][0]), "=&v"(a[1][0][1]), "=&v"(a[1][1][0]), "=&v"(a[1][1][1]), "=&v"(a[1][2][0]), "=&v"(a[1][2][1]), "=&v"(a[1][3][0]), "=&v"(a[1][3][1]), "=&v"(b[0][0]), "=&v"(b[0][1]), "=&v"(b[0][2]), "=&v"(b[0][3]), "=&v"(b[1][0]), "=&v"(b[1][1]), "=&v"(b[1][2]), "=&v"(b[1][3])
-                 : "v"(abase[0]), "v"(abase[1]), "v"(abase[2]), "v"(abase[3]), "v"(xbase)
+                 : "v"(abase[0]), "v"(abase[1]), "v"(abase[2]), "v"(abase[3]), "v"(xbase[0]), "v"(xbase[1])
                  : "memory");
 }
 
 template <>
-__device__ __forceinline__ void stage_reads<5>(const uint32_t (&abase)[4], uint32_t xbase, i16x4 (&a)[2][4][2],
-                                                 u32x4 (&b)[2][5])
+__device__ __forceinline__ void stage_reads<5>(const uint32_t (&abase)[4], const uint32_t (&xbase)[2],
+                                                 i16x4 (&a)[2][4][2], u32x4 (&b)[2][5])
 {
     asm volatile("ds_read_b64_tr_b16 %0, %26 offset:0\n\t"
                  "ds_read_b64_tr_b16 %1, %26 offset:512\n\t"
@@ -236,26 +243,26 @@ __device__ __forceinline__ void stage_reads<5>(const uint32_t (&abase)[4], uint3
                  "ds_read_b64_tr_b16 %6, %29 offset:0\n\t"
                  "ds_read_b64_tr_b16 %7, %29 offset:512\n\t"
                  "ds_read_b128 %16, %30 offset:0\n\t"
-                 "ds_read_b128 %17, %30 offset:1024\n\t"
-                 "ds_read_b128 %18, %30 offset:2048\n\t"
-                 "ds_read_b128 %19, %30 offset:3072\n\t"
-                 "ds_read_b128 %20, %30 offset:4096\n\t"
-                 "ds_read_b64_tr_b16 %8, %26 offset:24576\n\t"
-                 "ds_read_b64_tr_b16 %9, %26 offset:25088\n\t"
-                 "ds_read_b64_tr_b16 %10, %27 offset:24576\n\t"
-                 "ds_read_b64_tr_b16 %11, %27 offset:25088\n\t"
-                 "ds_read_b64_tr_b16 %12, %28 offset:24576\n\t"
-                 "ds_read_b64_tr_b16 %13, %28 offset:25088\n\t"
-                 "ds_read_b64_tr_b16 %14, %29 offset:24576\n\t"
-                 "ds_read_b64_tr_b16 %15, %29 offset:25088\n\t"
-                 "ds_read_b128 %21, %30 offset:24576\n\t"
-                 "ds_read_b128 %22, %30 offset:25600\n\t"
-                 "ds_read_b128 %23, %30 offset:26624\n\t"
-                 "ds_read_b128 %24, %30 offset:27648\n\t"
-                 "ds_read_b128 %25, %30 offset:28672\n\t"
+                 "ds_read_b128 %17, %30 offset:2048\n\t"
+                 "ds_read_b128 %18, %30 offset:4096\n\t"
+                 "ds_read_b128 %19, %30 offset:6144\n\t"
+                 "ds_read_b128 %20, %30 offset:8192\n\t"
+                 "ds_read_b64_tr_b16 %8, %26 offset:4096\n\t"
+                 "ds_read_b64_tr_b16 %9, %26 offset:4608\n\t"
+                 "ds_read_b64_tr_b16 %10, %27 offset:4096\n\t"
+                 "ds_read_b64_tr_b16 %11, %27 offset:4608\n\t"
+                 "ds_read_b64_tr_b16 %12, %28 offset:4096\n\t"
+                 "ds_read_b64_tr_b16 %13, %28 offset:4608\n\t"
+                 "ds_read_b64_tr_b16 %14, %29 offset:4096\n\t"
+                 "ds_read_b64_tr_b16 %15, %29 offset:4608\n\t"
+                 "ds_read_b128 %21, %31 offset:0\n\t"
+                 "ds_read_b128 %22, %31 offset:2048\n\t"
+                 "ds_read_b128 %23, %31 offset:4096\n\t"
+                 "ds_read_b128 %24, %31 offset:6144\n\t"
+                 "ds_read_b128 %25, %31 offset:8192\n\t"
                  "s_waitcnt lgkmcnt(0)"
                  : "=&v"(a[0][0][0]), "=&v"(a[0][0][1]), "=&v"(a[0][1][0]), "=&v"(a[0][1][1]), "=&v"(a[0][2][0]), "=&v"(a[0][2][1]), "=&v"(a[0][3][0]), "=&v"(a[0][3][1]), "=&v"(a[1][0][0]), "=&v"(a[1][0][1]), "=&v"(a[1][1][0]), "=&v"(a[1][1][1]), "=&v"(a[1][2][0]), "=&v"(a[1][2][1]), "=&v"(a[1][3][0]), "=&v"(a[1][3][1]), "=&v"(b[0][0]), "=&v"(b[0][1]), "=&v"(b[0][2]), "=&v"(b[0][3]), "=&v"(b[0][4]), "=&v"(b[1][0]), "=&v"(b[1][1]), "=&v"(b[1][2]), "=&v"(b[1][3]), "=&v"(b[1][4])
-                 : "v"(abase[0]), "v"(abase[1]), "v"(abase[2]), "v"(abase[3]), "v"(xbase)
+                 : "v"(abase[0]), "v"(abase[1]), "v"(abase[2]), "v"(abase[3]), "v"(xbase[0]), "v"(xbase[1])
                  : "memory");
 }
 
@@ -269,8 +276,8 @@ struct GemmArgs {
     int Cin, Cout;          // channels of one group
     int f_ld;               // F row length (output channels of all groups)
     int sh, sw, pt, pl, dh, dw;
-    int ksteps;             // KH * KW * (32-channel slices)
-    int nstages;            // ceil(ksteps / SPS)
+    int nstages;            // KH * KW * (64-channel slices)
+    int taps;               // KH * KW
     int m_total;            // N * Ho * Wo
     int n_tiles;            // 64-channel tiles per group
     int nt_all;             // n_tiles * groups: channel tiles per pixel tile
@@ -306,20 +313,25 @@ __global__ __launch_bounds__(GT) void dense_gemm_mfma(GemmArgs a)
     if (wave < LOADERS) {
         // ---- Loader wave p: issues its share of every stage's loads and
         // waits for them; the barrier then publishes the stage.
-        const int pw = wave;
+        // The wave index as a scalar: every LDS destination below is then
+        // computed on the scalar unit (M0), not moved out of a vector
+        // register per load.
+        const int pw = __builtin_amdgcn_readfirstlane(wave);
         const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<uint16_t *>(a.X), 0, (int)a.x_records, BUF_WORD3);
         const __amdgpu_buffer_rsrc_t fr = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<uint16_t *>(a.F), 0, (int)a.f_records, BUF_WORD3);
-        // Patch loads: load v of loader p fills tile pixels 16*(4v + p) ..+15,
-        // lane L taking pixel 16*(4v + p) + L/4 and stored chunk L % 4, which
-        // holds logical chunk (L % 4) ^ ((pixel / 4) % 4) (8 channels).
-        const int xchunk = (lane & 3) ^ ((lane >> 4) & 3);
-        int xb0[BPW], iy0[BPW], ix0[BPW];
-        bool mok[BPW];
+        // Patch loads: load v of loader p fills tile pixels
+        // 8*(LOADERS*v + p) ..+7, lane L taking pixel P = 8*(LOADERS*v + p) + L/8
+        // and stored chunk L % 8, which holds logical chunk
+        // (L % 8) ^ ((P >> 1) % 8) (8 channels): the same for every v.
+        constexpr int XL = S::XLOADS;
+        const int xchunk = (lane & 7) ^ ((4 * (pw & 1) + (lane >> 4)) & 7);
+        int xb0[XL], iy0[XL], ix0[XL];
+        bool mok[XL];
 #pragma unroll
-        for (int v = 0; v < BPW; ++v) {
-            const int m = m0 + 16 * (4 * v + pw) + (lane >> 2);
+        for (int v = 0; v < XL; ++v) {
+            const int m = m0 + 8 * (LOADERS * v + pw) + (lane >> 3);
             mok[v] = m < a.m_total;
             const uint32_t mm = mok[v] ? (uint32_t)m : 0u;
             const uint32_t ny = fdiv_g(mm, a.div_wo);
@@ -330,20 +342,21 @@ __global__ __launch_bounds__(GT) void dense_gemm_mfma(GemmArgs a)
             iy0[v] = y * a.sh - a.pt;
             ix0[v] = x * a.sw - a.pl;
         }
-        // Filter loads: loader p fills rows 8p .. 8p+7 of a step's slice,
-        // lane L row 8p + L/8, stored chunk L % 8 (logical chunk
-        // (L % 8) ^ fswz(row)).
+        // Filter loads: loader p fills rows 8p .. 8p+7 of the slice's 64, lane
+        // L row 8p + L/8, stored chunk L % 8 (logical chunk (L % 8) ^
+        // fswz(row)).
         const int frow = 8 * pw + (lane >> 3);
         const int fcol = o0 + 8 * ((lane & 7) ^ fswz(frow));
         const bool fcol_ok = fcol < a.Cout;
 
-        // The step whose loads go out next: tap (li, lj), channel slice lcs.
-        int lks = 0, lcs = 0, li = 0, lj = 0;
-        auto issue_step = [&](uint8_t *dst) __attribute__((always_inline)) {
-            const bool kok = lks < a.ksteps;
-            const int c = lcs * 32;
+        // The stage whose loads go out next: tap (li, lj), channel slice lcs.
+        int lst = 0, lcs = 0, li = 0, lj = 0;
+        auto issue_stage = [&](int t) __attribute__((always_inline)) {
+            uint8_t *dst = ring + (t % NSTAGE) * S::STAGE;
+            const bool kok = lst < a.nstages;
+            const int c = lcs * 64;
 #pragma unroll
-            for (int v = 0; v < BPW; ++v) {
+            for (int v = 0; v < XL; ++v) {
                 const int iy = iy0[v] + li * a.dh;
                 const int ix = ix0[v] + lj * a.dw;
                 const bool ok = kok && mok[v] && (unsigned)iy < (unsigned)a.H && (unsigned)ix < (unsigned)a.W &&
@@ -352,19 +365,20 @@ __global__ __launch_bounds__(GT) void dense_gemm_mfma(GemmArgs a)
                     ok ? ((uint32_t)xb0[v] + (uint32_t)iy * (uint32_t)a.xs1 + (uint32_t)ix * (uint32_t)a.xs2 + (uint32_t)c) * 2u
                        : OOB;
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    xr, (__attribute__((address_space(3))) void *)(dst + 1024 * (4 * v + pw)), 16, off, 0, 0, 0);
+                    xr, (__attribute__((address_space(3))) void *)(dst + 1024 * (LOADERS * v + pw)), 16, off, 0, 0, 0);
             }
             {
                 const int tap = li * a.KW + lj;
-                const bool ok = kok && fcol_ok && c + frow < a.Cin;
-                const uint32_t off = ok ? (uint32_t)((((int64_t)tap * a.Cin + c + frow) * a.f_ld + oc0 + fcol) * 2) : OOB;
+                const int row = c + frow;
+                const bool ok = kok && fcol_ok && row < a.Cin;
+                const uint32_t off = ok ? (uint32_t)((((int64_t)tap * a.Cin + row) * a.f_ld + oc0 + fcol) * 2) : OOB;
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    fr, (__attribute__((address_space(3))) void *)(dst + S::XSTEP + 1024 * pw), 16, off, 0, 0, 0);
+                    fr, (__attribute__((address_space(3))) void *)(dst + S::XSTAGE + 1024 * pw), 16, off, 0, 0, 0);
             }
-            // Next step: tap column, then tap row, then channel slice (the
+            // Next stage: tap column, then tap row, then channel slice (the
             // taps of one slice read neighbouring input lines while they are
             // cached).
-            ++lks;
+            ++lst;
             if (++lj == a.KW) {
                 lj = 0;
                 if (++li == a.KH) {
@@ -372,12 +386,6 @@ __global__ __launch_bounds__(GT) void dense_gemm_mfma(GemmArgs a)
                     ++lcs;
                 }
             }
-        };
-        auto issue_stage = [&](int t) __attribute__((always_inline)) {
-            uint8_t *dst = ring + (t % NSTAGE) * S::STAGE;
-#pragma unroll
-            for (int st = 0; st < SPS; ++st)
-                issue_step(dst + st * S::STEP);
         };
 
         issue_stage(0);
@@ -402,16 +410,20 @@ __global__ __launch_bounds__(GT) void dense_gemm_mfma(GemmArgs a)
 
     // ---- Computing wave w: MFMAs on the stage published by the barrier.
     const int cw = wave - LOADERS;
-    // Fragment addresses within a stage. Filter: lane (g, r) reads row
-    // 8g + 4h + r/4 (h = 0, 1), logical chunk 2nb + (r%4)/2, half r%2.
-    // Patch: block b of the wave, pixel 16*(cw*BPW + b) + r, logical chunk g.
+    // Fragment addresses within a stage. Filter, k-step s: lane (g, r) reads
+    // row 32s + 8g + 4h + r/4 (h = 0, 1), logical chunk 2nb + (r%4)/2, half
+    // r%2. Patch, k-step s: block b of the wave, pixel
+    // P = 16*(cw*BPW + b) + r, logical chunk 4s + g.
     const int arow = 8 * g + (r >> 2);
     const int asw = fswz(arow) >> 1;
     uint32_t abase0[4];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
-        abase0[nb] = (uint32_t)(S::XSTEP + 128 * arow + 32 * (nb ^ asw) + 16 * ((r & 3) >> 1) + 8 * (r & 1));
-    const uint32_t xbase0 = (uint32_t)(64 * (16 * cw * BPW + r) + 16 * (g ^ ((r >> 2) & 3)));
+        abase0[nb] = (uint32_t)(S::XSTAGE + 128 * arow + 32 * (nb ^ asw) + 16 * ((r & 3) >> 1) + 8 * (r & 1));
+    uint32_t xbase0[2];
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+        xbase0[st] = (uint32_t)(128 * (16 * cw * BPW + r) + 16 * ((4 * st + g) ^ ((r >> 1) & 7)));
     const uint32_t ring_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)ring;
 
     f32x4 acc[BPW][NB];
@@ -426,15 +438,22 @@ __global__ __launch_bounds__(GT) void dense_gemm_mfma(GemmArgs a)
         lds_barrier();
         __builtin_amdgcn_sched_barrier(0);
         const uint32_t sb = ring_lds + (uint32_t)((t % NSTAGE) * S::STAGE);
-        uint32_t ab[4];
+        uint32_t ab[4], xbs[2];
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
             ab[nb] = sb + abase0[nb];
+        xbs[0] = sb + xbase0[0];
+        xbs[1] = sb + xbase0[1];
         i16x4 fa[2][4][2];
         u32x4 xv[2][BPW];
-        stage_reads<BPW>(ab, sb + xbase0, fa, xv);
+        stage_reads<BPW>(ab, xbs, fa, xv);
+        // A slice of at most 32 channels (the last, when Cin is not a
+        // multiple of 64) has nothing in its second k-step.
+        const bool two = (t / a.taps) * 64 + 32 < a.Cin;
 #pragma unroll
-        for (int st = 0; st < SPS; ++st) {
+        for (int st = 0; st < 2; ++st) {
+            if (st == 1 && !two)
+                break;
             bf16x8 wf[NB];
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
@@ -617,8 +636,8 @@ hipError_t launch_dense_gemm_bf16(const DenseProblem &p, hipStream_t s)
     a.pl = p.pl;
     a.dh = p.dh;
     a.dw = p.dw;
-    a.ksteps = p.KH * p.KW * ((a.Cin + 31) / 32);
-    a.nstages = (a.ksteps + SPS - 1) / SPS;
+    a.taps = p.KH * p.KW;
+    a.nstages = a.taps * ((a.Cin + 63) / 64);
     a.m_total = p.N * p.Ho * p.Wo;
     a.n_tiles = (a.Cout + GN - 1) / GN;
     a.nt_all = a.n_tiles * p.groups;
