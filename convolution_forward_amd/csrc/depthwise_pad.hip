@@ -81,13 +81,14 @@ struct PadArgs {
     int tile_elems;    // LDS elements zeroed per tile (whole blocks plus slack)
     int cpr;           // 16-byte copy pieces per input row (W / 4)
     FastDiv div_bands, div_tpp, div_wo, div_cpr, div_rows;  // div_rows: rows copied per whole plane
+    FastDiv div_c;
 };
 
 // BATCH: 16-byte loads in flight per thread per copy round. Four cover
 // every tile of up to 1024 pieces in one round; larger tiles take eight
 // (fewer rounds) at the price of registers, i.e. of resident workgroups.
 template <int KH, int KW, int S, int RT, int BATCH, int EXACT>
-__global__ __launch_bounds__(THREADS) void dw_pad_kernel(PadArgs a)
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(8))) void dw_pad_kernel(PadArgs a)
 {
 #pragma clang fp contract(off)
     extern __shared__ __align__(16) float lds[];
@@ -106,7 +107,7 @@ __global__ __launch_bounds__(THREADS) void dw_pad_kernel(PadArgs a)
     const int iy_last = min(a.H, iy_top + a.RP);               // one past the last row copied
     const int nr = iy_last - iy_first;                          // input rows copied per plane
 
-    // The thread's task, decided first so the weight loads overlap the copy.
+    // The thread's task.
     const int p = (int)fdiv((uint32_t)tid, a.div_tpp);
     const int rem = tid - p * a.TPP;
     const int g = (int)fdiv((uint32_t)rem, a.div_wo);
@@ -114,11 +115,14 @@ __global__ __launch_bounds__(THREADS) void dw_pad_kernel(PadArgs a)
     const int oy0 = oy_lo + g * RT;
     const bool active = p < np && oy0 < oy_hi;
     const int q = q0 + (active ? p : 0);
-    const int oc = q % a.C;
-    float wv[KH * KW];
-#pragma unroll
-    for (int k = 0; k < KH * KW; ++k)
-        wv[k] = a.w[(int64_t)oc * (KH * KW) + k];
+    const int oc = (int)(q - fdiv((uint32_t)q, a.div_c) * (uint32_t)a.C);
+    constexpr int KK = KH * KW;
+    // The weights of the tile's planes sit in LDS behind the tile: one
+    // 4-byte load per weight, straight into LDS, issued behind the tile's
+    // first loads. Held in registers from the start they kept 25 registers
+    // busy through the copy (the 5x5 variants then did not fit 8 waves per
+    // SIMD).
+    float *wl = lds + a.tile_elems;
 
     // Copy: piece k of the tile is row k / cpr (of the np*nr rows, plane
     // major) and columns 4*(k % cpr) .. +3.
@@ -139,6 +143,20 @@ __global__ __launch_bounds__(THREADS) void dw_pad_kernel(PadArgs a)
             v[u] = __builtin_amdgcn_raw_buffer_load_b128(xr, k < npieces ? off : OOB, 0, 0);
         }
         if (base == 0) {
+            // Weight e of the tile is tap e % KK of plane q0 + e / KK, whose
+            // channel is the plane's index modulo C.
+            const __amdgpu_buffer_rsrc_t wr =
+                __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(a.w), 0, a.C * KK * 4, BUF_WORD3);
+            const int nw = np * KK;
+            for (int w0 = 0; w0 < nw; w0 += THREADS) {
+                const int e = w0 + tid;
+                const int pe = e / KK;
+                const int qe = q0 + (e < nw ? pe : 0);
+                const int ce = qe - (int)fdiv((uint32_t)qe, a.div_c) * a.C;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    wr, (__attribute__((address_space(3))) void *)(wl + w0 + (tid & ~63)), 4,
+                    e < nw ? (uint32_t)((ce * KK + e - pe * KK) * 4) : OOB, 0, 0, 0);
+            }
             // Zero the tile's blocks while the first loads are in flight.
             for (int e = tid * 4; e < a.tile_elems; e += THREADS * 4)
                 *reinterpret_cast<f32x4 *>(lds + e) = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -160,6 +178,10 @@ __global__ __launch_bounds__(THREADS) void dw_pad_kernel(PadArgs a)
     __syncthreads();
     if (!active)
         return;
+    float wv[KK];
+#pragma unroll
+    for (int k = 0; k < KK; ++k)
+        wv[k] = wl[p * KK + k];
 
     // Tap (ky, kx) of output row t: padded row g*RT*S + t*S + ky of block
     // p, padded column PL - pw + ox*S + kx.
@@ -192,6 +214,13 @@ __global__ __launch_bounds__(THREADS) void dw_pad_kernel(PadArgs a)
                 }
             }
         }
+        // One input row at a time: the row's sums are pinned here, so its
+        // inputs die before the next row is read. Left alone, the compiler
+        // reads every row ahead of the arithmetic (88 registers for the 5x5
+        // seven-row variant) and fewer workgroups fit a CU.
+#pragma unroll
+        for (int t = 0; t < RT; ++t)
+            asm volatile("" : "+v"(acc[t]));
     }
 
     const float bv = a.bias ? a.bias[oc] : 0.0f;
@@ -216,6 +245,7 @@ __global__ __launch_bounds__(THREADS) void dw_pad_kernel(PadArgs a)
 
 struct PadPlan {
     int RT, PPW, bands, RB, TPP, WP, RP, PS, tile_elems, batch;
+    int64_t lds_bytes;  // the tile's blocks and the weights of its planes
     double score;
 };
 
@@ -247,10 +277,13 @@ PadPlan pad_plan_for(const DwProblem &p, int RT)
     // (the last group may run past the band; those outputs are not stored).
     t.RP = (t.RB - 1) * S + p.KH;
     t.PS = t.RP * t.WP;
-    auto lds_for = [&](int ppw) { return (int64_t)ppw * t.PS + 4; };
-    while (t.PPW > 1 && lds_for(t.PPW) * 4 > LDS_LIMIT)
+    const int KK = p.KH * p.KW;
+    auto tile_for = [&](int ppw) { return ((int64_t)ppw * t.PS + 4 + 3) / 4 * 4; };
+    auto lds_for = [&](int ppw) { return (tile_for(ppw) + ((int64_t)ppw * KK + THREADS - 1) / THREADS * THREADS) * 4; };
+    while (t.PPW > 1 && lds_for(t.PPW) > LDS_LIMIT)
         --t.PPW;
-    t.tile_elems = (int)((lds_for(t.PPW) + 3) / 4 * 4);
+    t.tile_elems = (int)tile_for(t.PPW);
+    t.lds_bytes = lds_for(t.PPW);
     // 16-byte pieces of the largest tile: its planes, or its band's rows.
     const int64_t rows = t.PPW > 1 ? std::min<int64_t>(p.H, t.RP - p.ph) : std::min<int64_t>(p.H, t.RP);
     t.batch = (int64_t)t.PPW * rows * (p.W / 4) <= 4 * THREADS ? 4 : 8;
@@ -276,10 +309,12 @@ bool pad_plan(const DwProblem &p, PadPlan &out)
     const int64_t planes = (int64_t)p.N * p.C;
     if (planes >= (1ll << 31) - THREADS || planes * p.Ho * p.Wo >= (1ll << 40) || (int64_t)p.H * p.W >= (1ll << 28))
         return false;
+    if ((int64_t)p.C * p.KH * p.KW * 4 >= (1ll << 31))
+        return false;       // weight offsets are 32-bit
     bool have = false;
     for (int RT : {2, 4, 7}) {
         PadPlan t = pad_plan_for(p, RT);
-        if ((int64_t)t.tile_elems * 4 > LDS_LIMIT)
+        if (t.lds_bytes > LDS_LIMIT)
             continue;
         if ((int64_t)t.PPW * p.H * p.W * 4 >= (1ll << 31))
             continue;
@@ -360,11 +395,12 @@ hipError_t launch_dw_pad(const DwProblem &p, hipStream_t s)
     a.div_tpp = make_fastdiv((uint32_t)t.TPP);
     a.div_wo = make_fastdiv((uint32_t)p.Wo);
     a.div_cpr = make_fastdiv((uint32_t)a.cpr);
+    a.div_c = make_fastdiv((uint32_t)p.C);
     // Whole-plane tiles start at input row -ph: every tile copies the same
     // rows, min(H, RP - ph) of them.
     a.div_rows = make_fastdiv((uint32_t)std::max(1, std::min(p.H, t.RP - p.ph)));
     const int64_t tiles = ((int64_t)a.planes + t.PPW - 1) / t.PPW * t.bands;
-    const size_t lds = (size_t)t.tile_elems * 4;
+    const size_t lds = (size_t)t.lds_bytes;
     const bool exact = p.mode == CONV_DW_EXACT;
     if (p.KH == 3)
         return p.sh == 1 ? launch_pad_s<3, 3, 1>(a, t, (unsigned)tiles, lds, exact, s)
