@@ -38,6 +38,7 @@ EXTRA_FLAGS = {
     "depthwise_direct.hip": ["-ffp-contract=off"],
     "depthwise_tiled.hip": ["-ffp-contract=off"],
     "depthwise_pad.hip": ["-ffp-contract=off"],
+    "depthwise_planes.hip": ["-ffp-contract=off"],
 }
 
 

@@ -34,6 +34,7 @@
 #include <algorithm>
 
 #include "common.h"
+#include "fastdiv.h"
 #include "internal.h"
 
 namespace convfwd {
@@ -47,21 +48,6 @@ constexpr int PL = 4;                 // padded columns before the image (>= pw)
 constexpr uint32_t OOB = 0x80000000u;
 constexpr int BUF_WORD3 = 0x00020000;
 constexpr int LDS_LIMIT = 64 * 1024;
-
-struct FastDiv {
-    uint32_t m, s;
-};
-
-FastDiv make_fastdiv(uint32_t d)
-{
-    uint32_t s = 0;
-    while ((1ull << s) < d)
-        ++s;
-    const uint64_t m = ((1ull << 32) * ((1ull << s) - d)) / d + 1;
-    return FastDiv{(uint32_t)m, s};
-}
-
-__device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) { return (__umulhi(n, f.m) + n) >> f.s; }
 
 struct PadArgs {
     const float *X;

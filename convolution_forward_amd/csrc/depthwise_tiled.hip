@@ -29,11 +29,18 @@
 //  * Taps that fall in the padding read whatever neighbour sits in LDS and
 //    replace it with +0 before the multiply: the arithmetic sees exactly the
 //    zero the definition puts there.
-//  * The weights of the thread's plane stay in registers; the thread stores
-//    its RT outputs directly (neighbouring lanes write neighbouring words).
+//  * The weights of the tile's planes follow the tile into LDS, one 4-byte
+//    load straight into LDS per weight, issued behind the tile's first
+//    loads; after the copy each thread takes its plane's weights into
+//    registers.
+//  * The thread stores its RT outputs directly, with streaming stores
+//    (neighbouring lanes write neighbouring words of a row). Small planes
+//    (whole planes per workgroup) normally go to the kernel in
+//    depthwise_planes.hip; this one takes them only when that one declines.
 #include <algorithm>
 
 #include "common.h"
+#include "fastdiv.h"
 #include "internal.h"
 
 namespace convfwd {
@@ -50,22 +57,6 @@ constexpr uint32_t OOB = 0x80000000u;
 constexpr int BUF_WORD3 = 0x00020000;
 constexpr int LDS_LIMIT = 64 * 1024;
 
-// n / d for 0 <= n < 2^31 by multiply-high (division by an invariant integer).
-struct FastDiv {
-    uint32_t m, s;
-};
-
-FastDiv make_fastdiv(uint32_t d)
-{
-    uint32_t s = 0;
-    while ((1ull << s) < d)
-        ++s;
-    const uint64_t m = ((1ull << 32) * ((1ull << s) - d)) / d + 1;
-    return FastDiv{(uint32_t)m, s};
-}
-
-__device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) { return (__umulhi(n, f.m) + n) >> f.s; }
-
 struct TileArgs {
     const float *X;
     const float *w;
@@ -80,7 +71,9 @@ struct TileArgs {
     int RB;            // output rows per band
     int TPP;           // threads per plane: (row groups) * Wo
     int half;          // LDS elements per phase plane (stride 2)
-    FastDiv div_bands, div_tpp, div_wo, div_mult;
+    int wofs;          // LDS element where the tile's weights start
+    int HoWo;          // outputs per plane
+    FastDiv div_bands, div_tpp, div_wo, div_mult, div_cout;
 };
 
 template <int KH, int KW, int S, int RT, int EXACT>
@@ -117,11 +110,10 @@ __global__ __launch_bounds__(THREADS) void dw_tiled_kernel(TileArgs a)
     const bool active = p < a.PPW && q < qend && oy0 < oy_hi;
     const int qc = active ? q : q0;
     const int ip = (int)fdiv((uint32_t)qc, a.div_mult);
-    const int occ = qc % a.Cout;
-    float wv[KH * KW];
-#pragma unroll
-    for (int k = 0; k < KH * KW; ++k)
-        wv[k] = a.w[(int64_t)occ * (KH * KW) + k];
+    const int occ = qc - (int)fdiv((uint32_t)qc, a.div_cout) * a.Cout;
+    constexpr int KK = KH * KW;
+    float *wl = lds + a.wofs;
+    float bv = 0.0f;
 
     // Copy the tile range into LDS, BATCH chunks per thread per round: all
     // loads of a round are issued before the first write waits for them.
@@ -133,11 +125,32 @@ __global__ __launch_bounds__(THREADS) void dw_tiled_kernel(TileArgs a)
         f32x4 v[BATCH];
 #pragma unroll
         for (int u = 0; u < BATCH; ++u) {
-            const int k = base + tid + u * THREADS;
-            const int64_t e = a0 + 4 * (int64_t)k;
-            const bool ok = k < nchunks && e >= 0 && e < a.XE;
-            v[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                 xr, ok ? (uint32_t)((e - abase) * 4) : OOB, 0, 0));
+            // Slots past the range for the whole workgroup issue nothing.
+            if (base + u * THREADS < nchunks) {
+                const int k = base + tid + u * THREADS;
+                const int64_t e = a0 + 4 * (int64_t)k;
+                const bool ok = k < nchunks && e >= 0 && e < a.XE;
+                v[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                     xr, ok ? (uint32_t)((e - abase) * 4) : OOB, 0, 0));
+            }
+        }
+        if (base == 0) {
+            // Weight e of the tile is tap e % KK of plane q0 + e / KK, whose
+            // output channel is the plane's index modulo Cout.
+            const __amdgpu_buffer_rsrc_t wr =
+                __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(a.w), 0, a.Cout * KK * 4, BUF_WORD3);
+            const int nw = (qend - q0) * KK;
+            for (int w0 = 0; w0 < nw; w0 += THREADS) {
+                const int e = w0 + tid;
+                const int pe = e / KK;
+                const int qe = q0 + (e < nw ? pe : 0);
+                const int ce = qe - (int)fdiv((uint32_t)qe, a.div_cout) * a.Cout;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    wr, (__attribute__((address_space(3))) void *)(wl + w0 + (tid & ~63)), 4,
+                    e < nw ? (uint32_t)((ce * KK + e - pe * KK) * 4) : OOB, 0, 0, 0);
+            }
+            if (a.bias)
+                bv = a.bias[occ];
         }
 #pragma unroll
         for (int u = 0; u < BATCH; ++u) {
@@ -156,6 +169,15 @@ __global__ __launch_bounds__(THREADS) void dw_tiled_kernel(TileArgs a)
     if (!active)
         return;
 
+    float acc[RT];
+#pragma unroll
+    for (int t = 0; t < RT; ++t)
+        acc[t] = +0.0f;
+    float wv[KK];
+#pragma unroll
+    for (int k = 0; k < KK; ++k)
+        wv[k] = wl[p * KK + k];
+
     // Column validity of each tap (the same for every row).
     const int ix0 = ox * S - a.pw;
     bool cok[KW];
@@ -166,10 +188,6 @@ __global__ __launch_bounds__(THREADS) void dw_tiled_kernel(TileArgs a)
     // Input row iy of plane ip sits at LDS element (ip*HW + iy*W - a0) (stride
     // 1). Rows outside the plane are read from a clamped row and zeroed.
     const int plane_rel = (int)((int64_t)ip * a.HW - a0);
-    float acc[RT];
-#pragma unroll
-    for (int t = 0; t < RT; ++t)
-        acc[t] = +0.0f;
 
     constexpr int NIR = (RT - 1) * S + KH;     // input rows the thread's outputs read
 #pragma unroll
@@ -210,10 +228,16 @@ __global__ __launch_bounds__(THREADS) void dw_tiled_kernel(TileArgs a)
                 }
             }
         }
+        // One input row at a time (its sums pinned here), so the compiler
+        // does not read every row ahead of the arithmetic.
+#pragma unroll
+        for (int t = 0; t < RT; ++t)
+            asm volatile("" : "+v"(acc[t]));
     }
 
-    const float bv = a.bias ? a.bias[occ] : 0.0f;
-    float *yp = a.Y + (int64_t)q * a.Ho * a.Wo + ox;
+    // Direct streaming stores: neighbouring lanes write neighbouring words
+    // of an output row.
+    float *yp = a.Y + (int64_t)q * a.HoWo + ox;
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
         const int oy = oy0 + t;
@@ -223,7 +247,7 @@ __global__ __launch_bounds__(THREADS) void dw_tiled_kernel(TileArgs a)
                 r = r + bv;
             if (EXACT && __builtin_isnan(r))
                 r = __uint_as_float(0x7FC00000u);
-            yp[(int64_t)oy * a.Wo] = r;
+            __builtin_nontemporal_store(r, &yp[(int64_t)oy * a.Wo]);
         }
     }
 }
@@ -328,7 +352,8 @@ __global__ __launch_bounds__(THREADS) void dw_row1d_kernel(RowArgs1d a)
 
 struct TilePlan {
     int RT, PPW, bands, RB, TPP;
-    int64_t lds_elems;
+    int64_t tile_elems;  // the input range (with slack), a multiple of 4
+    int64_t lds_elems;   // tile and weights
     double util;        // fraction of thread-row slots that hold an output
     double score;       // util, discounted when the grid is too small to hide latency
 };
@@ -358,15 +383,17 @@ TilePlan plan_for(const DwProblem &p, int RT)
         t.bands = (p.Ho + t.RB - 1) / t.RB;
     }
     const int64_t HW = (int64_t)p.H * p.W;
-    auto lds_for = [&](int ppw) {
+    auto tile_for = [&](int ppw) {
         // q0/mult .. (q0+ppw-1)/mult: at most ceil((ppw-1)/mult) plane steps.
         const int64_t plane_steps = (ppw - 1 + p.mult - 1) / p.mult;
         const int64_t rows = std::min<int64_t>(p.H, (int64_t)(t.RB - 1) * S + p.KH);
         const int64_t elems = plane_steps * HW + rows * p.W + 8 + 2 * SLACK;
         return ((elems + 3) / 4) * 4;
     };
+    auto lds_for = [&](int ppw) { return tile_for(ppw) + (((int64_t)ppw * p.KH * p.KW + 3) / 4) * 4; };
     while (t.PPW > 1 && lds_for(t.PPW) * 4 > LDS_LIMIT)
         --t.PPW;
+    t.tile_elems = tile_for(t.PPW);
     t.lds_elems = lds_for(t.PPW);
     const int64_t planes = (int64_t)p.N * p.C * p.mult;
     const int64_t tiles = (planes + t.PPW - 1) / t.PPW * t.bands;
@@ -449,7 +476,8 @@ bool plan(const DwProblem &p, TilePlan &out)
     const int64_t planes = (int64_t)p.N * p.C * p.mult;
     if (XE % 4 != 0 || (reinterpret_cast<uintptr_t>(p.X) & 15) != 0)
         return false;       // 16-byte chunks must tile X exactly
-    if (planes >= (1ll << 31) - THREADS || planes * p.Ho * p.Wo >= (1ll << 40))
+    if (planes >= (1ll << 31) - THREADS || planes * p.Ho * p.Wo >= (1ll << 40) ||
+        (int64_t)p.Ho * p.Wo >= (1ll << 31) || (int64_t)p.C * p.mult * p.KH * p.KW * 4 >= (1ll << 31))
         return false;
     bool have = false;
     // Rows per thread: more rows reuse each LDS value for more outputs,
@@ -502,7 +530,7 @@ hipError_t launch_k(const TileArgs &a, int S, int RT, unsigned grid, size_t lds,
 bool dw_tiled_supports(const DwProblem &p)
 {
     TilePlan t;
-    return row1d_takes(p) || dw_pad_supports(p) || plan(p, t);
+    return row1d_takes(p) || dw_pad_supports(p) || dw_planes_supports(p) || plan(p, t);
 }
 
 hipError_t launch_dw_tiled(const DwProblem &p, hipStream_t s)
@@ -512,6 +540,9 @@ hipError_t launch_dw_tiled(const DwProblem &p, hipStream_t s)
     // Windows with the zero border in LDS (depthwise_pad.hip) when it fits.
     if (dw_pad_supports(p))
         return launch_dw_pad(p, s);
+    // Whole small planes with the zero border in LDS (depthwise_planes.hip).
+    if (dw_planes_supports(p))
+        return launch_dw_planes(p, s);
     TilePlan t;
     if (!plan(p, t))
         return hipErrorNotSupported;
@@ -534,8 +565,11 @@ hipError_t launch_dw_tiled(const DwProblem &p, hipStream_t s)
     a.bands = t.bands;
     a.RB = t.RB;
     a.TPP = t.TPP;
-    // Phase planes: half of the LDS range each (the range is a multiple of 4).
-    a.half = (int)(t.lds_elems / 2);
+    // Phase planes: half of the tile range each (the range is a multiple of 4).
+    a.half = (int)(t.tile_elems / 2);
+    a.wofs = (int)t.tile_elems;
+    a.HoWo = p.Ho * p.Wo;
+    a.div_cout = make_fastdiv((uint32_t)a.Cout);
     a.div_bands = make_fastdiv((uint32_t)t.bands);
     a.div_tpp = make_fastdiv((uint32_t)t.TPP);
     a.div_wo = make_fastdiv((uint32_t)p.Wo);

@@ -167,9 +167,13 @@ def test_auto_variant_queries(lib):
     for l in (wl.DW_5X5S2_EXACT, *wl.DW_SWEEP):
         v = dq_shape(lib, l.N, l.C, l.H, l.W, l.mult, l.KH, l.KW, l.stride, l.stride, l.pad, l.pad, l.dil, l.dil)
         assert v == cf.VARIANT_TILED, l.name
-    # ... but not from an input that is not 16-byte aligned
+    # An input that is not 16-byte aligned: planes small enough for whole
+    # planes per workgroup still run tiled (that kernel reads X four bytes at
+    # a time); the large-plane kernels need 16-byte rows and fall back.
     l = wl.DW_5X5S2_EXACT
-    assert dq_shape(lib, l.N, l.C, l.H, l.W, 1, 5, 5, 2, 2, 2, 2, 1, 1, X=XA + 4) == cf.VARIANT_DIRECT
+    assert dq_shape(lib, l.N, l.C, l.H, l.W, 1, 5, 5, 2, 2, 2, 2, 1, 1, X=XA + 4) == cf.VARIANT_TILED
+    l = wl.DW_SWEEP[0]
+    assert dq_shape(lib, l.N, l.C, l.H, l.W, 1, 3, 3, 1, 1, 1, 1, 1, 1, X=XA + 4) == cf.VARIANT_DIRECT
     # Shapes the tiled kernel does not take fall back to the direct kernel.
     assert dq_shape(lib, 2, 4, 11, 11, 3, 3, 3, 3, 3, 0, 0, 1, 1) == cf.VARIANT_DIRECT
     assert dq_shape(lib, 1, 2, 19, 23, 1, 3, 3, 1, 1, 2, 2, 2, 2) == cf.VARIANT_DIRECT

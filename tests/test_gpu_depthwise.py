@@ -200,3 +200,37 @@ def test_gpu_dw_write_coverage_and_determinism():
     assert not torch.isnan(y1).any()
     y2 = gpu_dw(X, w, stride=2, padding=2, mode="fast")
     assert torch.equal(y1.view(torch.int32), y2.view(torch.int32))
+
+
+# Small planes (whole planes per workgroup) from and into buffers that start
+# 4 bytes past a 16-byte boundary: the kernel reads X four bytes at a time
+# and falls back to 4-byte stores for a Y it cannot write in 16-byte pieces.
+UNALIGNED = [  # N, C, H, W, mult, K, stride, pad, bias
+    (2, 37, 7, 7, 1, 5, 1, 2, True),
+    (3, 5, 14, 14, 2, 5, 2, 2, False),
+    (2, 9, 9, 13, 1, 3, 1, 1, True),
+]
+
+
+@pytest.mark.parametrize("case", UNALIGNED)
+@pytest.mark.parametrize("mode", ["exact", "fast"])
+def test_gpu_dw_unaligned_buffers(case, mode):
+    N, C, H, W, m, K, s, p, has_bias = case
+    seed = 7000 + UNALIGNED.index(case)
+    X = wl.random_tensor((N, C, H, W), seed)
+    w = wl.random_tensor((C * m, K, K), seed + 1)
+    b = wl.random_tensor((C * m,), seed + 2) if has_bias else None
+    ref = oracle.depthwise_nchw(X, w, bias=b, stride=s, padding=p, mode=mode)
+    xbuf = torch.zeros(X.numel() + 1, device=DEV)
+    xv = xbuf[1:].view(X.shape)
+    xv.copy_(X.to(DEV))
+    ybuf = torch.full((ref.size + 1,), float("nan"), device=DEV)
+    yv = ybuf[1:].view(ref.shape)
+    wd = w.to(DEV)
+    bd = None if b is None else b.to(DEV)
+    assert xv.data_ptr() % 16 == 4 and yv.data_ptr() % 16 == 4
+    assert cf.depthwise_variant_for(xv, wd, s, p, exact=(mode == "exact"), bias=bd, out=yv) == cf.VARIANT_TILED
+    cf.conv_depthwise(xv, wd, bias=bd, stride=s, padding=p, exact=(mode == "exact"), out=yv)
+    torch.cuda.synchronize()
+    assert_same_bits(yv, ref, mode)
+    assert torch.isnan(ybuf[0]).item()          # nothing written before Y
