@@ -39,6 +39,7 @@ EXTRA_FLAGS = {
     "depthwise_tiled.hip": ["-ffp-contract=off"],
     "depthwise_pad.hip": ["-ffp-contract=off"],
     "depthwise_planes.hip": ["-ffp-contract=off"],
+    "depthwise_rows.hip": ["-ffp-contract=off"],
 }
 
 

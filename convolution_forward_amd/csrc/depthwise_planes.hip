@@ -35,6 +35,7 @@
 #include <algorithm>
 
 #include "common.h"
+#include "dw_range_store.h"
 #include "fastdiv.h"
 #include "internal.h"
 
@@ -254,35 +255,7 @@ __global__ __launch_bounds__(THREADS) void dw_planes_kernel(PlaneArgs a)
         }
     }
     __syncthreads();
-    if (a.y_aligned) {
-        // Pieces c = tid, tid + THREADS, ...: all read, then all stored.
-        // Only the first and the last piece can be partial.
-        constexpr int NPC = (THREADS * RT + 3 + 4 * THREADS - 1) / (4 * THREADS);
-        float *yb = a.Y + (ostart - lead);
-        const int end = lead + olen;
-        f32x4 ov[NPC];
-#pragma unroll
-        for (int i = 0; i < NPC; ++i) {
-            const int e0 = 4 * (tid + i * THREADS);
-            if (e0 < end)
-                ov[i] = *reinterpret_cast<const f32x4 *>(lds + e0);
-        }
-#pragma unroll
-        for (int i = 0; i < NPC; ++i) {
-            const int e0 = 4 * (tid + i * THREADS);
-            if (e0 >= lead && e0 + 4 <= end) {
-                __builtin_nontemporal_store(ov[i], reinterpret_cast<f32x4 *>(yb + e0));
-            } else if (e0 < end) {
-#pragma unroll
-                for (int k = 0; k < 4; ++k)
-                    if (e0 + k >= lead && e0 + k < end)
-                        yb[e0 + k] = ov[i][k];
-            }
-        }
-    } else {
-        for (int e = tid; e < olen; e += THREADS)
-            __builtin_nontemporal_store(lds[e], &a.Y[ostart + e]);
-    }
+    store_range_from_lds<THREADS, THREADS * RT + 3>(lds, a.Y, ostart, olen, lead, a.y_aligned, tid);
 }
 
 // --- host side -------------------------------------------------------------

@@ -530,7 +530,7 @@ hipError_t launch_k(const TileArgs &a, int S, int RT, unsigned grid, size_t lds,
 bool dw_tiled_supports(const DwProblem &p)
 {
     TilePlan t;
-    return row1d_takes(p) || dw_pad_supports(p) || dw_planes_supports(p) || plan(p, t);
+    return row1d_takes(p) || dw_pad_supports(p) || dw_rows_supports(p) || dw_planes_supports(p) || plan(p, t);
 }
 
 hipError_t launch_dw_tiled(const DwProblem &p, hipStream_t s)
@@ -540,7 +540,11 @@ hipError_t launch_dw_tiled(const DwProblem &p, hipStream_t s)
     // Windows with the zero border in LDS (depthwise_pad.hip) when it fits.
     if (dw_pad_supports(p))
         return launch_dw_pad(p, s);
-    // Whole small planes with the zero border in LDS (depthwise_planes.hip).
+    // 7- and 14-wide planes with "same" padding, a row per thread
+    // (depthwise_rows.hip).
+    if (dw_rows_supports(p))
+        return launch_dw_rows(p, s);
+    // Other small planes with the zero border in LDS (depthwise_planes.hip).
     if (dw_planes_supports(p))
         return launch_dw_planes(p, s);
     TilePlan t;

@@ -64,6 +64,8 @@ hipError_t launch_dw_direct(const DwProblem &p, hipStream_t s);
 bool dw_tiled_supports(const DwProblem &p);
 bool dw_pad_supports(const DwProblem &p);
 bool dw_planes_supports(const DwProblem &p);
+bool dw_rows_supports(const DwProblem &p);
+hipError_t launch_dw_rows(const DwProblem &p, hipStream_t s);
 hipError_t launch_dw_planes(const DwProblem &p, hipStream_t s);
 hipError_t launch_dw_pad(const DwProblem &p, hipStream_t s);
 hipError_t launch_dw_tiled(const DwProblem &p, hipStream_t s);
