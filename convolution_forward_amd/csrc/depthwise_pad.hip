@@ -120,13 +120,16 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(8))) vo
         u32x4 v[BATCH];
 #pragma unroll
         for (int u = 0; u < BATCH; ++u) {
-            const int k = base + tid + u * THREADS;
-            const int row = (int)fdiv((uint32_t)k, a.div_cpr);
-            const int cx = k - row * a.cpr;
-            const int pp = a.PPW > 1 ? (int)fdiv((uint32_t)row, a.div_rows) : 0;  // whole planes: nr is fixed
-            const int rr = row - pp * nr;
-            const uint32_t off = (uint32_t)(((int64_t)pp * a.HW + (int64_t)rr * a.W + cx * 4) * 4);
-            v[u] = __builtin_amdgcn_raw_buffer_load_b128(xr, k < npieces ? off : OOB, 0, 0);
+            // Slots past the tile for the whole workgroup issue nothing.
+            if (base + u * THREADS < npieces) {
+                const int k = base + tid + u * THREADS;
+                const int row = (int)fdiv((uint32_t)k, a.div_cpr);
+                const int cx = k - row * a.cpr;
+                const int pp = a.PPW > 1 ? (int)fdiv((uint32_t)row, a.div_rows) : 0;  // whole planes: nr is fixed
+                const int rr = row - pp * nr;
+                const uint32_t off = (uint32_t)(((int64_t)pp * a.HW + (int64_t)rr * a.W + cx * 4) * 4);
+                v[u] = __builtin_amdgcn_raw_buffer_load_b128(xr, k < npieces ? off : OOB, 0, 0);
+            }
         }
         if (base == 0) {
             // Weight e of the tile is tap e % KK of plane q0 + e / KK, whose
