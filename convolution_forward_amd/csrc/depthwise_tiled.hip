@@ -530,13 +530,17 @@ hipError_t launch_k(const TileArgs &a, int S, int RT, unsigned grid, size_t lds,
 bool dw_tiled_supports(const DwProblem &p)
 {
     TilePlan t;
-    return row1d_takes(p) || dw_pad_supports(p) || dw_rows_supports(p) || dw_planes_supports(p) || plan(p, t);
+    return row1d_takes(p) || dw_waves_supports(p) || dw_pad_supports(p) || dw_rows_supports(p) || dw_planes_supports(p) || plan(p, t);
 }
 
 hipError_t launch_dw_tiled(const DwProblem &p, hipStream_t s)
 {
     if (row1d_takes(p))
         return launch_row1d(p, s);
+    // Stride-2 windows on rows of at most 64 outputs: one task per wave, no
+    // workgroup barrier (depthwise_waves.hip).
+    if (dw_waves_supports(p))
+        return launch_dw_waves(p, s);
     // Windows with the zero border in LDS (depthwise_pad.hip) when it fits.
     if (dw_pad_supports(p))
         return launch_dw_pad(p, s);

@@ -63,6 +63,8 @@ hipError_t launch_dense_gemm_f32(const DenseProblem &p, hipStream_t s);
 hipError_t launch_dw_direct(const DwProblem &p, hipStream_t s);
 bool dw_tiled_supports(const DwProblem &p);
 bool dw_pad_supports(const DwProblem &p);
+bool dw_waves_supports(const DwProblem &p);
+hipError_t launch_dw_waves(const DwProblem &p, hipStream_t s);
 bool dw_planes_supports(const DwProblem &p);
 bool dw_rows_supports(const DwProblem &p);
 hipError_t launch_dw_rows(const DwProblem &p, hipStream_t s);

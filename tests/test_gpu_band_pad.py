@@ -93,6 +93,7 @@ PADDED = [  # N, C, H, W, K, stride, pad, bias
     (1, 2, 120, 64, 3, 1, 1, False),       # bands of rows, last one ragged
     (4, 6, 28, 28, 5, 1, 2, True),         # the 28x28 layer shape, bias
     (2, 8, 56, 56, 5, 2, 2, False),        # the exact-mode workload's plane shape
+    (1, 3, 40, 136, 5, 2, 2, True),        # stride 2 with 68 output columns (rows past 64 stay on this kernel)
 ]
 
 
