@@ -31,6 +31,25 @@ __device__ __forceinline__ void store_from_f32(uint16_t *p, float v) { *p = f32_
 // before its first launch there. Only a success is remembered (one bit per
 // device and kernel), so a failed attempt is made again by the next call;
 // later calls (graph capture included) then make no HIP call at all.
+// Bring every 64-byte line of a kernel's argument block (up to 256 bytes)
+// into the scalar cache with one batch of scalar loads at the kernel's
+// start: x passes through an asm that takes one word of each line as input,
+// so everything computed from the returned value waits for that one batch.
+// Left alone, the compiler loads each argument just before its first use,
+// behind the branches that need the earlier ones, so a kernel paid one
+// memory round trip per such step before its first global load. The asm is
+// not volatile and touches no memory, so loads after it can still be proven
+// free of stores (uniform loads then stay scalar loads).
+template <class T>
+__device__ __forceinline__ int with_args_loaded(int x, const T &a)
+{
+    static_assert(sizeof(T) <= 256, "four lines at most");
+    const uint32_t *p = reinterpret_cast<const uint32_t *>(&a);
+    constexpr int L = (int)(sizeof(T) / 4) - 1;
+    asm("" : "+s"(x) : "s"(p[0]), "s"(p[16 < L ? 16 : L]), "s"(p[32 < L ? 32 : L]), "s"(p[48 < L ? 48 : L]));
+    return x;
+}
+
 template <auto Kern>
 hipError_t allow_lds(int bytes)
 {

@@ -286,9 +286,10 @@ void dense_band_mfma(BandArgs a)
     // runs on XCD s % 8). Slot s takes band (s % 8) * (bands/8) + (s/8) /
     // tiles and tile (s/8) % tiles, so all tiles of a band and neighbouring
     // bands of an image share one XCD's L2 (the halo rows meet there).
+    const int bid = with_args_loaded((int)blockIdx.x, a);
     const int tiles_all = a.tiles * a.groups;
-    const int slot_in_xcd = (int)(blockIdx.x >> 3);
-    const int band = (int)(blockIdx.x & 7) * (int)(gridDim.x >> 3) / tiles_all + slot_in_xcd / tiles_all;
+    const int slot_in_xcd = bid >> 3;
+    const int band = (bid & 7) * (int)(gridDim.x >> 3) / tiles_all + slot_in_xcd / tiles_all;
     const int tile = slot_in_xcd % tiles_all;
     const int grp = tile / a.tiles;
     const int o0 = (tile - grp * a.tiles) * TILE_O;

@@ -300,7 +300,8 @@ __global__ __launch_bounds__(GT) void dense_gemm_mfma(GemmArgs a)
     const int r = lane & 15;
     // Slot s runs on XCD s % 8; consecutive tiles (the channel tiles of one
     // pixel tile first) go to one XCD so the X rows they share meet in its L2.
-    const int tile = (int)(blockIdx.x & 7) * (int)(gridDim.x >> 3) + (int)(blockIdx.x >> 3);
+    const int bid = with_args_loaded((int)blockIdx.x, a);
+    const int tile = (bid & 7) * (int)(gridDim.x >> 3) + (bid >> 3);
     if (tile >= a.tiles)
         return;
     const int mt = tile / a.nt_all;

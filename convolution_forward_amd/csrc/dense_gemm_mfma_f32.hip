@@ -90,7 +90,7 @@ __global__ __launch_bounds__(GT) void dense_gemm_mfma_f32(GemmArgsF a)
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int tile = (int)blockIdx.x;
+    const int tile = with_args_loaded((int)blockIdx.x, a);
     const int mt = tile / a.ntiles;
     const int o0 = (tile - mt * a.ntiles) * TN;
     const int m0 = mt * TM;

@@ -311,8 +311,9 @@ void dense_rows_mfma(RowArgs a)
     // image then run on one XCD, so the input rows they share (the whole band
     // across tiles, the halo rows across bands) meet in that XCD's L2.
     const int tiles_all = a.tiles * a.groups;
-    const int slot_in_xcd = (int)(blockIdx.x >> 3);
-    const int band = (int)(blockIdx.x & 7) * (int)(gridDim.x >> 3) / tiles_all + slot_in_xcd / tiles_all;
+    const int bid = with_args_loaded((int)blockIdx.x, a);
+    const int slot_in_xcd = bid >> 3;
+    const int band = (bid & 7) * (int)(gridDim.x >> 3) / tiles_all + slot_in_xcd / tiles_all;
     const int tile = slot_in_xcd % tiles_all;
     const int grp = tile / a.tiles;
     const int o0 = (tile - grp * a.tiles) * COUT_TILE;   // within the group

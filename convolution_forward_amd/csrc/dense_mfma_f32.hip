@@ -123,8 +123,9 @@ void dense_rows_mfma_f32(RowArgsF a)
     const int pg = wave >> 2;           // pixel-block group 0..1
     // Slot s runs on XCD s % 8; all tiles of a band and neighbouring bands
     // share an XCD (same map as the bf16 kernel).
-    const int slot_in_xcd = (int)(blockIdx.x >> 3);
-    const int band = (int)(blockIdx.x & 7) * (int)(gridDim.x >> 3) / a.tiles + slot_in_xcd / a.tiles;
+    const int bid = with_args_loaded((int)blockIdx.x, a);
+    const int slot_in_xcd = bid >> 3;
+    const int band = (bid & 7) * (int)(gridDim.x >> 3) / a.tiles + slot_in_xcd / a.tiles;
     const int o0 = (slot_in_xcd % a.tiles) * COUT_TILE;
     if (band >= a.bands)
         return;

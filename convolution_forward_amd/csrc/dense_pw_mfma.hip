@@ -195,8 +195,9 @@ void dense_pw_mfma(PwArgs a)
     const int wave = tid >> 6;
     // Slot s runs on XCD s % 8; the channel tiles of one pixel range share
     // an XCD, so their common input meets in that XCD's L2.
-    const int slot_in_xcd = (int)(blockIdx.x >> 3);
-    const int mt = (int)(blockIdx.x & 7) * (a.mtiles >> 3) + slot_in_xcd / a.ctiles;
+    const int bid = with_args_loaded((int)blockIdx.x, a);
+    const int slot_in_xcd = bid >> 3;
+    const int mt = (bid & 7) * (a.mtiles >> 3) + slot_in_xcd / a.ctiles;
     const int ct = slot_in_xcd % a.ctiles;
     if (mt >= a.mreal)
         return;

@@ -82,8 +82,9 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(8))) vo
 
     // Tile: output planes [q0, qend), output rows [oy_lo, oy_hi). Padded
     // row 0 of every block is input row iy_top.
-    const uint32_t tile = fdiv(blockIdx.x, a.div_bands);
-    const int band = (int)(blockIdx.x - tile * (uint32_t)a.bands);
+    const uint32_t bid = (uint32_t)with_args_loaded((int)blockIdx.x, a);
+    const uint32_t tile = fdiv(bid, a.div_bands);
+    const int band = (int)(bid - tile * (uint32_t)a.bands);
     const int q0 = (int)tile * a.PPW;
     const int np = min(a.PPW, a.planes - q0);
     const int oy_lo = band * a.RB;

@@ -71,7 +71,7 @@ __global__ __launch_bounds__(THREADS) void dw_rows_kernel(RowsArgs a)
     const int tid = threadIdx.x;
 
     // Output planes [q0, qend) read input planes [ip0, ip0 + nip).
-    const int q0 = (int)blockIdx.x * a.PPW;
+    const int q0 = with_args_loaded((int)blockIdx.x, a) * a.PPW;
     const int qend = min(q0 + a.PPW, a.planes);
     const int ip0 = (int)fdiv((uint32_t)q0, a.div_mult);
     const int nip = (int)fdiv((uint32_t)(qend - 1), a.div_mult) - ip0 + 1;

@@ -84,8 +84,9 @@ __global__ __launch_bounds__(THREADS) void dw_tiled_kernel(TileArgs a)
     const int tid = threadIdx.x;
 
     // Tile: output planes [q0, qend), output rows [oy_lo, oy_hi).
-    const uint32_t tile = fdiv(blockIdx.x, a.div_bands);
-    const int band = (int)(blockIdx.x - tile * (uint32_t)a.bands);
+    const uint32_t bid = (uint32_t)with_args_loaded((int)blockIdx.x, a);
+    const uint32_t tile = fdiv(bid, a.div_bands);
+    const int band = (int)(bid - tile * (uint32_t)a.bands);
     const int q0 = (int)tile * a.PPW;
     const int qend = min(q0 + a.PPW, a.planes);
     const int oy_lo = band * a.RB;
@@ -282,8 +283,9 @@ __global__ __launch_bounds__(THREADS) void dw_row1d_kernel(RowArgs1d a)
     extern __shared__ __align__(16) float lds[];
     const int tid = threadIdx.x;
     // Output row (n, oc, oy) and segment.
-    const uint32_t row = fdiv(blockIdx.x, a.div_segs);
-    const int seg = (int)(blockIdx.x - row * (uint32_t)a.segs);
+    const uint32_t bid = (uint32_t)with_args_loaded((int)blockIdx.x, a);
+    const uint32_t row = fdiv(bid, a.div_segs);
+    const int seg = (int)(bid - row * (uint32_t)a.segs);
     const uint32_t plane = fdiv(row, a.div_ho);            // n * Cout + oc
     const int oy = (int)(row - plane * (uint32_t)a.Ho);
     const uint32_t n = fdiv(plane, a.div_cout);
