@@ -18,7 +18,8 @@
 // per input word of the window rows; the copy is one division per element
 // (which plane), since each plane's rows sit in LDS as they sit in X, after
 // ph zero rows.
-//  * A workgroup takes PPW = 256 / Ho whole output planes; thread tid owns
+//  * A workgroup of NT threads (256, or 128 for 14-wide planes) takes
+//    PPW = NT / Ho whole output planes; thread tid owns
 //    output row tid % Ho of tile plane tid / Ho.
 //  * The planes' pitch in LDS is chosen on the host so that the row starts
 //    of the 64 lanes of a wave fall on as few shared banks as possible.
@@ -36,7 +37,11 @@ namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int THREADS = 256;
+// Threads per workgroup: 256 for the 7-wide planes, 128 for the 14-wide
+// ones (half as many planes per workgroup, twice as many workgroups: the
+// 672-channel 5x5/2 layer 7.55 -> 7.20 us; the 960-channel 7-wide layer is
+// 1.5 % slower that way and 12 % slower with 512).
+constexpr int threads_for(int W) { return W == 14 ? 128 : 256; }
 constexpr int BATCH = 8;             // 4-byte loads in flight per thread per round
 constexpr int BATCH4 = 4;            // 16-byte loads in flight per thread per round
 constexpr uint32_t OOB = 0x80000000u;
@@ -59,8 +64,8 @@ struct RowsArgs {
     FastDiv div_ho, div_mult, div_cout, div_hw;
 };
 
-template <int W, int K, int S, int EXACT>
-__global__ __launch_bounds__(THREADS) void dw_rows_kernel(RowsArgs a)
+template <int W, int K, int S, int EXACT, int NT>
+__global__ __launch_bounds__(NT) void dw_rows_kernel(RowsArgs a)
 {
 #pragma clang fp contract(off)
     extern __shared__ __align__(16) float lds[];
@@ -100,7 +105,7 @@ __global__ __launch_bounds__(THREADS) void dw_rows_kernel(RowsArgs a)
             wv[k] = a.w[(int64_t)occ * KK + k];
         if (a.bias)
             bv = a.bias[occ];
-        for (int e = tid * 4; e < a.zero_words; e += THREADS * 4)
+        for (int e = tid * 4; e < a.zero_words; e += NT * 4)
             *reinterpret_cast<f32x4 *>(lds + e) = f32x4{0.f, 0.f, 0.f, 0.f};
         __syncthreads();
     };
@@ -114,8 +119,8 @@ __global__ __launch_bounds__(THREADS) void dw_rows_kernel(RowsArgs a)
         auto issue = [&](int base, f32x4 *v) {
 #pragma unroll
             for (int u = 0; u < BATCH4; ++u) {
-                const int k = base + u * THREADS + tid;
-                if (base + u * THREADS < nch)
+                const int k = base + u * NT + tid;
+                if (base + u * NT < nch)
                     v[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
                                                          cr, k < nch ? (uint32_t)k * 16 : OOB, 0, 0));
             }
@@ -123,8 +128,8 @@ __global__ __launch_bounds__(THREADS) void dw_rows_kernel(RowsArgs a)
         auto place = [&](int base, const f32x4 *v) {
 #pragma unroll
             for (int u = 0; u < BATCH4; ++u) {
-                const int k = base + u * THREADS + tid;
-                if (base + u * THREADS < nch && k < nch) {
+                const int k = base + u * NT + tid;
+                if (base + u * NT < nch && k < nch) {
                     // One division per piece: the plane of its first element,
                     // and how many of its elements stay in that plane.
                     const int j0 = 4 * k - lead;
@@ -158,7 +163,7 @@ __global__ __launch_bounds__(THREADS) void dw_rows_kernel(RowsArgs a)
         issue(0, v);
         behind_first_loads();
         place(0, v);
-        for (int base = THREADS * BATCH4; base < nch; base += THREADS * BATCH4) {
+        for (int base = NT * BATCH4; base < nch; base += NT * BATCH4) {
             issue(base, v);
             place(base, v);
         }
@@ -168,16 +173,16 @@ __global__ __launch_bounds__(THREADS) void dw_rows_kernel(RowsArgs a)
         auto issue = [&](int base, float *v) {
 #pragma unroll
             for (int u = 0; u < BATCH; ++u) {
-                const int j = base + u * THREADS + tid;
-                if (base + u * THREADS < nelem)
+                const int j = base + u * NT + tid;
+                if (base + u * NT < nelem)
                     v[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(xr, j < nelem ? (uint32_t)j * 4 : OOB, 0, 0));
             }
         };
         auto place = [&](int base, const float *v) {
 #pragma unroll
             for (int u = 0; u < BATCH; ++u) {
-                const int j = base + u * THREADS + tid;
-                if (base + u * THREADS < nelem && j < nelem) {
+                const int j = base + u * NT + tid;
+                if (base + u * NT < nelem && j < nelem) {
                     const int pl = (int)fdiv((uint32_t)j, a.div_hw);
                     lds[j + pl * gap + top] = v[u];
                 }
@@ -187,7 +192,7 @@ __global__ __launch_bounds__(THREADS) void dw_rows_kernel(RowsArgs a)
         issue(0, v);
         behind_first_loads();
         place(0, v);
-        for (int base = THREADS * BATCH; base < nelem; base += THREADS * BATCH) {
+        for (int base = NT * BATCH; base < nelem; base += NT * BATCH) {
             issue(base, v);
             place(base, v);
         }
@@ -244,7 +249,7 @@ __global__ __launch_bounds__(THREADS) void dw_rows_kernel(RowsArgs a)
         }
     }
     __syncthreads();
-    store_range_from_lds<THREADS, THREADS * WO + 3>(lds, a.Y, ostart, olen, lead, a.y_aligned, tid);
+    store_range_from_lds<NT, NT * WO + 3>(lds, a.Y, ostart, olen, lead, a.y_aligned, tid);
 }
 
 // --- host side -------------------------------------------------------------
@@ -256,10 +261,10 @@ struct RowsPlan {
 
 // The most lanes of one wave whose row start falls on one bank, for plane
 // pitch pp (thread tid reads from word (tid / Ho) * pp + (tid % Ho) * S * W).
-int worst_bank_share(int pp, int Ho, int S, int W, int ppw)
+int worst_bank_share(int pp, int Ho, int S, int W, int ppw, int nt)
 {
     int worst = 0;
-    for (int w0 = 0; w0 < THREADS; w0 += 64) {
+    for (int w0 = 0; w0 < nt; w0 += 64) {
         int count[BANKS] = {};
         for (int t = w0; t < w0 + 64; ++t) {
             const int p = t / Ho, oy = t % Ho;
@@ -283,10 +288,11 @@ bool rows_plan(const DwProblem &p, RowsPlan &t)
         return false;       // "same" columns; every output window overlaps the input
     const int S = p.sh;
     const int WO = (p.W + 2 * (K / 2) - K) / S + 1;
-    if (p.Wo != WO || p.Ho < 1 || p.Ho * 2 > THREADS)
+    const int nt = threads_for(p.W);
+    if (p.Wo != WO || p.Ho < 1 || p.Ho * 2 > nt)
         return false;
     const int64_t planes = (int64_t)p.N * p.C * p.mult;
-    if (planes >= (1ll << 31) - THREADS || planes * p.Ho * p.Wo >= (1ll << 40) ||
+    if (planes >= (1ll << 31) - nt || planes * p.Ho * p.Wo >= (1ll << 40) ||
         (int64_t)p.C * p.mult * K * K >= (1ll << 31) || (int64_t)p.H * p.W >= (1ll << 24) ||
         (int64_t)p.N * p.C * p.H * p.W >= (1ll << 40))
         return false;
@@ -294,10 +300,10 @@ bool rows_plan(const DwProblem &p, RowsPlan &t)
     // the last row an output reads.
     const int rows = std::max(p.H + p.ph, (p.Ho - 1) * S + K);
     const int pp0 = rows * p.W;
-    t.PPW = THREADS / p.Ho;
+    t.PPW = nt / p.Ho;
     int best = 1 << 30;
     for (int pp = pp0; pp < pp0 + BANKS; ++pp) {
-        const int share = worst_bank_share(pp, p.Ho, S, p.W, t.PPW);
+        const int share = worst_bank_share(pp, p.Ho, S, p.W, t.PPW, nt);
         if (share < best) {
             best = share;
             t.PP = pp;
@@ -306,7 +312,7 @@ bool rows_plan(const DwProblem &p, RowsPlan &t)
     auto words_for = [&](int ppw) {
         const int64_t nip = (ppw - 1 + p.mult - 1) / p.mult + 1;
         const int64_t in = ((nip * t.PP + 3) / 4) * 4;
-        return std::max<int64_t>(in, (int64_t)THREADS * WO + 4);
+        return std::max<int64_t>(in, (int64_t)nt * WO + 4);
     };
     while (t.PPW > 2 && words_for(t.PPW) * 4 > LDS_LIMIT)
         --t.PPW;
@@ -319,10 +325,11 @@ bool rows_plan(const DwProblem &p, RowsPlan &t)
 template <int W, int K, int S>
 hipError_t launch_wks(const RowsArgs &a, unsigned grid, size_t lds, bool exact, hipStream_t s)
 {
+    constexpr int NT = threads_for(W);
     if (exact)
-        hipLaunchKernelGGL((dw_rows_kernel<W, K, S, 1>), dim3(grid), dim3(THREADS), lds, s, a);
+        hipLaunchKernelGGL((dw_rows_kernel<W, K, S, 1, NT>), dim3(grid), dim3(NT), lds, s, a);
     else
-        hipLaunchKernelGGL((dw_rows_kernel<W, K, S, 0>), dim3(grid), dim3(THREADS), lds, s, a);
+        hipLaunchKernelGGL((dw_rows_kernel<W, K, S, 0, NT>), dim3(grid), dim3(NT), lds, s, a);
     return hipGetLastError();
 }
 

@@ -116,6 +116,9 @@ TILED = [  # N, C, H, W, mult, K, stride, pad, bias
     (4, 37, 7, 8, 1, 5, 1, 2, False),         # tiles of 36 planes, 148 planes
     (1, 1, 250, 250, 1, 3, 1, 1, False),      # widest rows the kernel takes
     (1, 2, 226, 226, 1, 3, 2, 1, True),       # stride 2 onto 113 columns
+    (2, 20, 14, 14, 1, 5, 2, 2, True),        # 14-wide rows, 128 threads: 18 planes a tile, 40 planes
+    (1, 11, 14, 14, 1, 3, 1, 1, False),       # 14 output rows: 9 planes a tile, a partial second tile
+    (3, 7, 14, 14, 2, 3, 2, 1, False),        # 14-wide rows with multiplier 2
 ]
 
 
