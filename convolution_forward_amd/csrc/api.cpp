@@ -207,9 +207,14 @@ bool dense_tiled_supports(const DenseProblem &p)
 // kernel of the operand type.
 hipError_t launch_dense_tiled(const DenseProblem &p, hipStream_t s)
 {
-    if (p.xdt != CONV_BF16)
+    if (p.xdt != CONV_BF16) {
+        // fp32 1x1 layers: three bf16 parts per value on the bf16 matrix
+        // cores (dense_pw_f32x6.hip).
+        if (dense_f32x6_supports(p))
+            return launch_dense_f32x6(p, s);
         return plain_window(p) && dense_mfma_f32_supports(p) ? launch_dense_mfma_f32(p, s)
                                                               : launch_dense_gemm_f32(p, s);
+    }
     // Strided windows whose groups fill 64-channel tiles: the GEMM kernel
     // (3x3 stride 2 -> 128 channels: 10.9 us against 16.9 on the row
     // kernel). Narrower groups stay with the row kernel's block-diagonal

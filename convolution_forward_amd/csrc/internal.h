@@ -57,6 +57,8 @@ hipError_t launch_dense_gemm_bf16(const DenseProblem &p, hipStream_t s);
 bool dense_mfma_f32_supports(const DenseProblem &p);
 hipError_t launch_dense_mfma_f32(const DenseProblem &p, hipStream_t s);
 bool dense_gemm_f32_supports(const DenseProblem &p);
+bool dense_f32x6_supports(const DenseProblem &p);
+hipError_t launch_dense_f32x6(const DenseProblem &p, hipStream_t s);
 hipError_t launch_dense_gemm_f32(const DenseProblem &p, hipStream_t s);
 
 // Depthwise kernels.
