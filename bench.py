@@ -542,6 +542,13 @@ def main():
             torch.cuda.empty_cache()
             cp = copy_context(by, args.mode, steps2, warmup, trials)
             secondary.append(dense_line(name, m, n, fl, by, peak, copies=cp))
+            if name == "dense1x1_f32":
+                # fp32 operands on the bf16 matrix cores: three bf16 parts per
+                # value, six part products per fp32 product.
+                tf = fl / (m * 1e-3) / 1e12
+                secondary[-1]["path"] = "bf16 matrix cores, fp32 values split into three bf16 parts, six products"
+                secondary[-1]["split_peak_TFLOP/s"] = round(BF16_MFMA_PEAK_TFLOPS / 6, 1)
+                secondary[-1]["frac_split_peak"] = round(tf / (BF16_MFMA_PEAK_TFLOPS / 6), 4)
         if want("im2col"):
             # The explicit im2col route on the headline layer (packing included).
             r, fl, by, cols_bytes = im2col_route_runner(wl.DENSE_3X3_BF16, args.mode)
