@@ -24,11 +24,13 @@
 // middle part is inf - inf). Non-finite outputs stay non-finite and finite
 // ones finite.
 //
-// Work: a workgroup (4 waves) owns 128 pixels x 128 output channels; wave w
-// computes pixels 64 (w & 1) .. +63 x channels 64 (w >> 1) .. +63 as 4 x 4
-// tiles of 16 x 16. The input channels go in chunks of 32: each chunk of X
-// and F is loaded into registers (16-byte loads, two chunks ahead: the
-// one after it is multiplied), split, and written to LDS as three bf16
+// Work: a workgroup (4 waves) owns 208 pixels (13 blocks of 16) x 128 output
+// channels; wave w computes every pixel block x channels 32 w .. +31 as
+// 13 x 2 tiles of 16 x 16. At the 1x1 workload that is 121 x 4 = 484
+// workgroups, one round at two per compute unit (128-pixel tiles made 784,
+// 1.53 rounds). The input channels go in chunks of 32: each chunk of X
+// and F is loaded into registers (16-byte loads, one chunk ahead, while
+// the current one is multiplied), split, and written to LDS as three bf16
 // planes of each: X as [pixel][channel] (B operand, 16-byte reads), F as
 // [channel][output] (A operand, gfx950 transposed reads).
 #include "common.h"
@@ -45,7 +47,8 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int BT = 256;
-constexpr int TP = 128;                 // pixels per tile
+constexpr int PB = 13;                  // 16-pixel blocks per tile
+constexpr int TP = 16 * PB;             // pixel slots per tile (208)
 constexpr int TO = 128;                 // output channels per tile
 constexpr int KC = 32;                  // input channels per chunk
 constexpr int XP = KC + 8;              // LDS pitch of a staged pixel (80 bytes: 16 lanes on distinct banks)
@@ -104,6 +107,7 @@ __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     if (pt >= a.ptiles)
         return;
     const int p0 = pt * TP;
+    const int pend = min(a.npix, p0 + TP);     // one past the tile's last pixel
     const int o0 = ot * TO;
 
     const __amdgpu_buffer_rsrc_t xr =
@@ -112,17 +116,20 @@ __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(a.F), 0, a.Cin * a.Cout * 4, BUF_WORD3);
     const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(a.Y, 0, (int)a.y_records, BUF_WORD3);
 
-    // Chunk loads: X unit u = tid + 256 i is pixel u / 8, channels 4 (u % 8)
-    // of the chunk; F unit u is chunk channel u / 32, outputs 4 (u % 32).
-    // Two register sets: chunk k + 2 loads while chunk k is multiplied.
-    u32x4 xa[4], fa[4], xb2[4], fb2[4];
-    auto load = [&](const int k0, u32x4 (&xv)[4], u32x4 (&fv)[4]) __attribute__((always_inline)) {
+    // Chunk loads: X unit u = tid + 256 i (u < 8 TP) is pixel u / 8,
+    // channels 4 (u % 8) of the chunk; F unit u is chunk channel u / 32,
+    // outputs 4 (u % 32). Chunk k + 1 loads while chunk k is multiplied (a
+    // second register set, two chunks ahead, did not fit beside the 104
+    // accumulator registers without spilling).
+    constexpr int XU = (8 * TP + BT - 1) / BT;      // X loads per thread
+    u32x4 xa[XU], fa[4];
+    auto load = [&](const int k0, u32x4 (&xv)[XU], u32x4 (&fv)[4]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < XU; ++i) {
             const int u = tid + BT * i;
             const int px = p0 + (u >> 3);
             const int c = k0 + 4 * (u & 7);
-            const bool ok = px < a.npix && c < a.Cin;
+            const bool ok = u < 8 * TP && px < pend && c < a.Cin;
             xv[i] = __builtin_amdgcn_raw_buffer_load_b128(xr, ok ? (uint32_t)(px * a.xs + c) * 4u : OOB, 0, 0);
         }
 #pragma unroll
@@ -134,16 +141,18 @@ __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
             fv[i] = __builtin_amdgcn_raw_buffer_load_b128(fr, ok ? (uint32_t)(c * a.Cout + o) * 4u : OOB, 0, 0);
         }
     };
-    auto stage = [&](const u32x4 (&xv)[4], const u32x4 (&fv)[4]) __attribute__((always_inline)) {
+    auto stage = [&](const u32x4 (&xv)[XU], const u32x4 (&fv)[4]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < XU; ++i) {
             const int u = tid + BT * i;
-            u32x2 h, m, l;
-            split4(xv[i], h, m, l);
-            uint16_t *d = xl + (u >> 3) * XP + 4 * (u & 7);
-            *reinterpret_cast<u32x2 *>(d) = h;
-            *reinterpret_cast<u32x2 *>(d + XPART) = m;
-            *reinterpret_cast<u32x2 *>(d + 2 * XPART) = l;
+            if (u < 8 * TP) {
+                u32x2 h, m, l;
+                split4(xv[i], h, m, l);
+                uint16_t *d = xl + (u >> 3) * XP + 4 * (u & 7);
+                *reinterpret_cast<u32x2 *>(d) = h;
+                *reinterpret_cast<u32x2 *>(d + XPART) = m;
+                *reinterpret_cast<u32x2 *>(d + 2 * XPART) = l;
+            }
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -157,97 +166,87 @@ __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         }
     };
 
-    const int ph = wave & 1;            // the wave's 64 pixels
-    const int oh = wave >> 1;           // the wave's 64 output channels
+    const int oq = wave;                // the wave's 32 output channels: 32 oq .. +31
     const int g = lane >> 4;            // k-group: chunk channels 8g .. 8g + 7
     const int r = lane & 15;
-    f32x4 acc[4][4];
+    f32x4 acc[PB][2];
 #pragma unroll
-    for (int pb = 0; pb < 4; ++pb)
+    for (int pb = 0; pb < PB; ++pb)
 #pragma unroll
-        for (int ob = 0; ob < 4; ++ob)
+        for (int ob = 0; ob < 2; ++ob)
             acc[pb][ob] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // Chunk k: stage it (after every wave is done with chunk k - 1), then
-    // request chunk k + 2 into the set just freed, then multiply.
     auto compute = [&]() __attribute__((always_inline)) {
-        // B fragments: pixel (64 ph + 16 pb + r), chunk channels 8g .. 8g + 7.
-        bf16x8 xb[4][3];
+        // A fragments of output channels 32 oq + 16 ob + (0..15): within each
+        // 16-lane group of the transposed read, lane r addresses row r / 4
+        // and columns 4 (r % 4) .. +3 of a 4-row block and receives four
+        // consecutive chunk channels of output channel r; two reads give
+        // the lane's eight.
+        bf16x8 wa[2][3];
 #pragma unroll
-        for (int pb = 0; pb < 4; ++pb)
-#pragma unroll
-            for (int q = 0; q < 3; ++q)
-                xb[pb][q] = *reinterpret_cast<const bf16x8 *>(xl + q * XPART + (ph * 64 + pb * 16 + r) * XP + 8 * g);
-#pragma unroll
-        for (int ob = 0; ob < 4; ++ob) {
-            // A fragments of output channels 64 oh + 16 ob + (0..15): within
-            // each 16-lane group of the transposed read, lane r addresses row
-            // r / 4 and columns 4 (r % 4) .. +3 of a 4-row block and receives
-            // four consecutive chunk channels of output channel r; two reads
-            // give the lane's eight.
-            bf16x8 wa[3];
+        for (int ob = 0; ob < 2; ++ob)
 #pragma unroll
             for (int q = 0; q < 3; ++q) {
                 i16x4 part[2];
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh) {
                     const int c = g * 8 + hh * 4 + (r >> 2);
-                    const int o = oh * 64 + ob * 16 + 4 * (r & 3);
+                    const int o = oq * 32 + ob * 16 + 4 * (r & 3);
                     part[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                         (__attribute__((address_space(3))) i16x4 *)(fl + q * FPART + c * FP + o));
                 }
                 const i16x8 both = {part[0][0], part[0][1], part[0][2], part[0][3],
                                     part[1][0], part[1][1], part[1][2], part[1][3]};
-                wa[q] = __builtin_bit_cast(bf16x8, both);
+                wa[ob][q] = __builtin_bit_cast(bf16x8, both);
             }
 #pragma unroll
-            for (int pb = 0; pb < 4; ++pb) {
+        for (int pb = 0; pb < PB; ++pb) {
+            // B fragments: pixel 16 pb + r of the tile, chunk channels 8g .. 8g + 7.
+            bf16x8 xb[3];
+#pragma unroll
+            for (int q = 0; q < 3; ++q)
+                xb[q] = *reinterpret_cast<const bf16x8 *>(xl + q * XPART + (pb * 16 + r) * XP + 8 * g);
+#pragma unroll
+            for (int ob = 0; ob < 2; ++ob) {
                 // Smallest products first.
                 f32x4 t = acc[pb][ob];
-                t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[2], xb[pb][0], t, 0, 0, 0);   // l * h
-                t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[1], xb[pb][1], t, 0, 0, 0);   // m * m
-                t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[0], xb[pb][2], t, 0, 0, 0);   // h * l
-                t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[1], xb[pb][0], t, 0, 0, 0);   // m * h
-                t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[0], xb[pb][1], t, 0, 0, 0);   // h * m
-                t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[0], xb[pb][0], t, 0, 0, 0);   // h * h
+                t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[ob][2], xb[0], t, 0, 0, 0);   // l * h
+                t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[ob][1], xb[1], t, 0, 0, 0);   // m * m
+                t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[ob][0], xb[2], t, 0, 0, 0);   // h * l
+                t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[ob][1], xb[0], t, 0, 0, 0);   // m * h
+                t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[ob][0], xb[1], t, 0, 0, 0);   // h * m
+                t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[ob][0], xb[0], t, 0, 0, 0);   // h * h
                 acc[pb][ob] = t;
             }
         }
     };
-    auto step = [&](const int k, const int nk, u32x4 (&xv)[4], u32x4 (&fv)[4]) __attribute__((always_inline)) {
-        if (k > 0)
-            __syncthreads();
-        stage(xv, fv);
-        __syncthreads();
-        if (k + 2 < nk)
-            load((k + 2) * KC, xv, fv);
-        compute();
-    };
     const int nk = (a.Cin + KC - 1) / KC;
     load(0, xa, fa);
-    if (nk > 1)
-        load(KC, xb2, fb2);
-    for (int k = 0; k < nk; k += 2) {
-        step(k, nk, xa, fa);
+    for (int k = 0; k < nk; ++k) {
+        if (k > 0)
+            __syncthreads();            // every wave is done with chunk k - 1
+        stage(xa, fa);
+        __syncthreads();
         if (k + 1 < nk)
-            step(k + 1, nk, xb2, fb2);
+            load((k + 1) * KC, xa, fa);
+        compute();
     }
 
-    // Lane (g, r) of tile (pb, ob) holds output channels 64 oh + 16 ob + 4 g
-    // + (0..3) of pixel 64 ph + 16 pb + r: one 16-byte store each.
+    // Lane (g, r) of tile (pb, ob) holds output channels 32 oq + 16 ob + 4 g
+    // + (0..3) of pixel 16 pb + r of the tile: one 16-byte store each.
 #pragma unroll
-    for (int ob = 0; ob < 4; ++ob) {
-        const int o = o0 + oh * 64 + ob * 16 + 4 * g;
+    for (int ob = 0; ob < 2; ++ob) {
+        const int o = o0 + oq * 32 + ob * 16 + 4 * g;
         f32x4 bv = {0.f, 0.f, 0.f, 0.f};
         if (a.bias && o < a.Cout)
             bv = *reinterpret_cast<const f32x4 *>(a.bias + o);
 #pragma unroll
-        for (int pb = 0; pb < 4; ++pb) {
-            const int px = p0 + ph * 64 + pb * 16 + r;
+        for (int pb = 0; pb < PB; ++pb) {
+            const int px = p0 + pb * 16 + r;
             const f32x4 v = acc[pb][ob];
             const u32x4 w = {__float_as_uint(v[0] + bv[0]), __float_as_uint(v[1] + bv[1]),
                              __float_as_uint(v[2] + bv[2]), __float_as_uint(v[3] + bv[3])};
-            const bool ok = px < a.npix && o < a.Cout;
+            const bool ok = px < pend && o < a.Cout;
             __builtin_amdgcn_raw_buffer_store_b128(w, yr, ok ? (uint32_t)(px * a.ys + o) * 4u : OOB, 0, 0);
         }
     }
@@ -276,8 +275,8 @@ bool plan_f32x6(const DenseProblem &p, F32x6Plan *pl)
         ((npix - 1) * p.ys[2] + p.Cout) * 4 >= (int64_t(1) << 31) || (int64_t)p.Cin * p.Cout * 4 >= (1ll << 31))
         return false;
     pl->npix = npix;
-    pl->ptiles = (int)((npix + TP - 1) / TP);
     pl->otiles = (p.Cout + TO - 1) / TO;
+    pl->ptiles = (int)((npix + TP - 1) / TP);
     return (int64_t)pl->ptiles * pl->otiles + 8 < (1ll << 31);
 }
 
