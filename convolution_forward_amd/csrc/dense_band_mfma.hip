@@ -152,14 +152,20 @@ __device__ __forceinline__ void static_for(Fn &&fn)
     }
 }
 
-template <int KH, int KW, int CS, int NR, int LS, bool OUT_BF16, int LR, int LT>
+template <int KH, int KW, int CS, int NR, int LS, bool OUT_BF16, int LR, int LT, bool GS>
 struct BandShape {
     static constexpr int CINP = 32 * CS;
+    // Small groups packed block-diagonally into a 64-channel tile (GS): the
+    // 32 output channels of wave half h belong to the groups whose inputs are
+    // channels 32h..32h+31, so the wave runs only that channel step of each
+    // tap; the other step's filter entries are all zero.
+    static_assert(!GS || CS == 2, "packed groups fill a 64-channel tile");
+    static constexpr int CSW = GS ? 1 : CS;                 // channel steps per tap a wave runs
     static constexpr int CG = CINP / 8;                     // 16-byte units per pixel
     static constexpr int SH = CS == 2 ? 1 : 2;              // log2(pixels per 256 bytes)
     static constexpr int FROW = KW * CINP * FPITCH;         // elements of one staged filter row
     static constexpr int FITEMS = (KW * CINP * 8 + BT - 1) / BT;  // 16-byte filter loads per thread per filter row
-    static constexpr int KSR = KW * CS;                     // k-steps per filter row
+    static constexpr int KSR = KW * CSW;                    // k-steps per filter row and wave
     static constexpr int TRN = KSR * NBW * 2;               // transposed reads per filter row
     static constexpr int RMAX = NR - KH + 1;                // output rows a band holds
     static constexpr int EARLY = NR < 3 ? NR : 3;           // input rows requested before filter rows 1..KH-1
@@ -216,7 +222,7 @@ struct TrOff {
     static constexpr int at(int q)
     {
         const int h = q & 1, nb = (q >> 1) % NBW, kk = q / (2 * NBW);
-        const int j = kk / (B::CINP / 32), cs = kk % (B::CINP / 32);
+        const int j = kk / B::CSW, cs = kk % B::CSW;
         return (I & 1) * B::FROW * 2 + ((j * B::CINP + cs * 32 + h * 4) * FPITCH + nb * 16) * 2;
     }
 };
@@ -260,11 +266,11 @@ __device__ __forceinline__ void tr_reads(uint32_t base, i16x4 (&p)[B::TRN])
 
 #undef CF_TR
 
-template <int KH, int KW, int CS, int NR, int SAUX, int LS, bool OUT_BF16, int LR, int LT>
+template <int KH, int KW, int CS, int NR, int SAUX, int LS, bool OUT_BF16, int LR, int LT, bool GS>
 __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void dense_band_mfma(BandArgs a)
 {
-    using B = BandShape<KH, KW, CS, NR, LS, OUT_BF16, LR, LT>;
+    using B = BandShape<KH, KW, CS, NR, LS, OUT_BF16, LR, LT, GS>;
     constexpr int ESZ = OUT_BF16 ? 2 : 4;
     constexpr int CINP = B::CINP;
     constexpr int CG = B::CG;
@@ -364,10 +370,12 @@ void dense_band_mfma(BandArgs a)
     // columns 4*(r%4)..+3 of a 4-row block and receives four consecutive
     // input channels of output channel r % 16 (the A-operand layout); two
     // reads give the lane's 8 channels. All reads of a filter row go out in
-    // one block with one wait (see tr_reads).
+    // one block with one wait (see tr_reads). With packed groups the wave's
+    // channel step (32 * half) is part of the base.
     bf16x8 wf[KH * KSR][NBW];
     const uint32_t fbase = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t *)farea +
-                           (uint32_t)((((lane >> 4) * 8 + ((lane & 15) >> 2)) * FPITCH + half * 32 + 4 * (lane & 3)) * 2);
+                           (uint32_t)((((lane >> 4) * 8 + ((lane & 15) >> 2) + (GS ? half * 32 : 0)) * FPITCH +
+                                       half * 32 + 4 * (lane & 3)) * 2);
     auto read_frow = [&](auto I) __attribute__((always_inline)) {
         constexpr int i = decltype(I)::value;
         i16x4 p[B::TRN];
@@ -437,15 +445,16 @@ void dense_band_mfma(BandArgs a)
 
     // X fragments of staged row r for this wave's 16-pixel block: for each
     // tap column j and 32-channel step, lane (g, p) reads chunk 4*cs + g of
-    // pixel slot x + j (x = its output pixel, clamped into the row).
+    // pixel slot x + j (x = its output pixel, clamped into the row). With
+    // packed groups the wave's one step is cs = half.
     const int x = pg * 16 + (lane & 15);
     const int xl = min(x, a.Wo - 1);
     auto read_x = [&](const int r, bf16x8 (&xb)[KSR]) __attribute__((always_inline)) {
         const uint8_t *row = xrows + r * ROW_BYTES;
 #pragma unroll
         for (int jc = 0; jc < KSR; ++jc) {
-            const int j = jc / CS;
-            const int cs = jc % CS;
+            const int j = jc / B::CSW;
+            const int cs = GS ? half : jc % B::CSW;
             const int p = xl + j;
             const int c = cs * 4 + (lane >> 4);
             const int unit = p * CG + (c ^ ((p >> B::SH) & (CG - 1)));
@@ -580,12 +589,12 @@ void dense_band_mfma(BandArgs a)
 // Defaults measured on the 3x3 layers: rows 6..8 requested at step 1 (so
 // that rows 3..5 reach the memory system first), barriers through step 3,
 // stores with the sc1 and nt policies (SAUX = 16 | 2).
-template <int KH, int KW, int CS, int NR, bool OB, int SAUX = 18, int LS = 3, int LR = 6, int LT = 1>
+template <int KH, int KW, int CS, int NR, bool OB, bool GS = false, int SAUX = 18, int LS = 3, int LR = 6, int LT = 1>
 hipError_t launch_band(const BandArgs &a, dim3 grid, hipStream_t s)
 {
-    auto kern = dense_band_mfma<KH, KW, CS, NR, SAUX, LS, OB, LR, LT>;
-    constexpr size_t lds = BandShape<KH, KW, CS, NR, LS, OB, LR, LT>::LDS;
-    const hipError_t attr = allow_lds<dense_band_mfma<KH, KW, CS, NR, SAUX, LS, OB, LR, LT>>((int)lds);
+    auto kern = dense_band_mfma<KH, KW, CS, NR, SAUX, LS, OB, LR, LT, GS>;
+    constexpr size_t lds = BandShape<KH, KW, CS, NR, LS, OB, LR, LT, GS>::LDS;
+    const hipError_t attr = allow_lds<dense_band_mfma<KH, KW, CS, NR, SAUX, LS, OB, LR, LT, GS>>((int)lds);
     if (attr != hipSuccess)
         return attr;
     hipLaunchKernelGGL(kern, grid, dim3(BT), lds, s, a);
@@ -690,6 +699,13 @@ hipError_t launch_dense_band(const DenseProblem &p, int gpack, hipStream_t s)
     if (slots >= (int64_t(1) << 31))
         return hipErrorNotSupported;
     const dim3 grid((unsigned)slots);
+    if (gpack != 0) {
+        // pack_groups makes 64-channel tiles: two channel steps per tap.
+        if (plan.CS != 2 || a.Cin != 64 || a.Cout != 64)
+            return hipErrorNotSupported;
+        return p.ydt == CONV_BF16 ? launch_band<3, 3, 2, BAND_NR, true, true>(a, grid, s)
+                                  : launch_band<3, 3, 2, BAND_NR, false, true>(a, grid, s);
+    }
     if (p.ydt == CONV_BF16)
         return plan.CS == 1 ? launch_band<3, 3, 1, BAND_NR, true>(a, grid, s)
                             : launch_band<3, 3, 2, BAND_NR, true>(a, grid, s);

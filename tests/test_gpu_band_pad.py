@@ -34,6 +34,8 @@ BAND = [
     (2, 11, 19, 48, 72, 1, 1, False),      # 48 of 64 channels, a second tile of 8
     (4, 12, 14, 128, 128, 1, 8, True),     # 8 groups of 16 packed block-diagonally
     (2, 10, 10, 64, 64, 1, 2, False),      # 2 groups of 32 packed
+    (4, 12, 14, 128, 128, 1, 16, False),   # 16 groups of 8 packed: each wave runs one channel step per tap
+    (3, 9, 20, 128, 128, 0, 4, True),      # 4 groups of 32 over two packed tiles
     (1, 3, 5, 64, 64, 0, 1, False),        # one output row, three pixels
 ]
 
@@ -68,6 +70,25 @@ def test_gpu_band_kernel_integer_bitwise():
     y = cf.conv2d_nhwc(X.to(DEV), F.to(DEV), padding=1)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(y.float().cpu().numpy(), ref.astype(np.float32))
+
+
+@pytest.mark.parametrize("groups", [4, 8, 16])
+def test_gpu_band_kernel_grouped_integer_bitwise(groups):
+    """Packed small groups (32, 16 and 8 channels), bf16 and fp32 outputs:
+    integer-valued sums are exact whatever the order, so every output must
+    equal the oracle's per-group sum, and no group may see another's input
+    channels or weights."""
+    g = torch.Generator().manual_seed(7150 + groups)
+    X = torch.randint(-2, 3, (4, 11, 13, 128), generator=g).to(torch.bfloat16)
+    F = torch.randint(-1, 2, (3, 3, 128 // groups, 128), generator=g).to(torch.bfloat16)
+    ref = oracle.conv2d_nhwc(X, F, padding=1, groups=groups)
+    assert np.max(np.abs(ref)) <= 256
+    for odt in (torch.bfloat16, torch.float32):
+        out = torch.full((4, 11, 13, 128), float("nan"), dtype=odt, device=DEV)
+        assert cf.dense_variant_for(X.to(DEV), F.to(DEV), padding=1, groups=groups, out=out) == cf.VARIANT_TILED
+        y = cf.conv2d_nhwc(X.to(DEV), F.to(DEV), padding=1, groups=groups, out=out)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(y.float().cpu().numpy(), ref.astype(np.float32))
 
 
 def test_gpu_band_kernel_repeat_and_coverage():
