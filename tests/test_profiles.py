@@ -57,11 +57,11 @@ def test_trace_summary_names_the_launched_headline_kernel():
         txt = fh.read()
     with open(bench.HEADLINE_SOURCE) as fh:
         src = fh.read()
-    m = re.search(r"template <int KH, int KW, int CS, int NR, bool OB, int SAUX = (\d+), int LS = (\d+), "
-                  r"int LR = (\d+), int LT = (\d+)>", src)
+    m = re.search(r"template <int KH, int KW, int CS, int NR, bool OB, bool GS = false, int SAUX = (\d+), "
+                  r"int LS = (\d+), int LR = (\d+), int LT = (\d+)>", src)
     assert m, "launcher defaults not found"
     saux, ls, lr, lt = m.groups()
-    assert f"kernel: dense_band_mfma<3, 3, 2, 9, {saux}, {ls}, true, {lr}, {lt}>" in txt
+    assert f"kernel: dense_band_mfma<3, 3, 2, 9, {saux}, {ls}, true, {lr}, {lt}, false>" in txt
     # bench.py's per-launch time without the profiler (launch gaps included)
     # against the traced kernel mean: tracing lengthens the kernels, never
     # by more than a quarter here, and the gaps cannot make a launch shorter
