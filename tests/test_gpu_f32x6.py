@@ -5,9 +5,11 @@ summed in fp32) against the fp64 CPU oracle.
 The bar is the fp32 one: max |g - r| / max |r| <= 1e-5. Integer-valued
 inputs up to 2^8 have no middle or low parts, so their sums are exact and
 must match bit for bit. Infinities and NaNs keep their class. The cases hit
-the tile edges: pixels that do not fill a 128-pixel tile, output channels
+the tile edges: pixels that do not fill a 208-pixel tile, output channels
 that do not fill a 128-channel tile, input channels that do not fill a
-32-channel chunk, pixel strides of a channel slice, bias.
+32-channel chunk, pixel strides of a channel slice, bias; and grids of more
+than one round of workgroups (an odd number of chunks, ragged pixel and
+channel tiles).
 """
 import numpy as np
 import pytest
@@ -26,7 +28,9 @@ CASES = [  # N, H, W, Cin, Cout, bias
     (4, 10, 13, 256, 512, True),     # four channel tiles, bias
     (1, 5, 9, 36, 64, False),        # 36 input channels: a partial second chunk
     (3, 8, 8, 4, 4, True),           # the smallest channel counts the kernel takes
-    (8, 28, 28, 64, 128, False),     # 6272 pixels, 49 tiles
+    (8, 28, 28, 64, 128, False),     # 6272 pixels, 31 tiles
+    (3, 37, 37, 36, 3600, True),     # 20 x 29 = 580 tiles (past one round), ragged pixel and channel tiles, bias
+    (4, 44, 44, 68, 2048, False),    # 38 x 16 = 608 tiles, three chunks (the last of 4 channels)
 ]
 
 
