@@ -57,6 +57,12 @@ constexpr int XPART = TP * XP;          // elements of one X plane
 constexpr int FPART = KC * FP;          // elements of one F plane
 constexpr size_t LDS_BYTES = (size_t)(3 * XPART + 3 * FPART) * 2;
 constexpr uint32_t OOB = 0x80000000u;
+// Output stores: device-scope write-through with the streaming hint (sc1 |
+// nt). Every workgroup finishes its products at about the same time and the
+// output (two thirds of the layer's bytes) then drains at once: 47.0 ->
+// 42.4 us at the 1x1 workload against the default policy (nt alone 43.5,
+// sc1 alone 44.2).
+constexpr int SAUX = 18;
 constexpr int BUF_WORD3 = 0x00020000;
 
 struct F32x6Args {
@@ -247,7 +253,7 @@ __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
             const u32x4 w = {__float_as_uint(v[0] + bv[0]), __float_as_uint(v[1] + bv[1]),
                              __float_as_uint(v[2] + bv[2]), __float_as_uint(v[3] + bv[3])};
             const bool ok = px < pend && o < a.Cout;
-            __builtin_amdgcn_raw_buffer_store_b128(w, yr, ok ? (uint32_t)(px * a.ys + o) * 4u : OOB, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(w, yr, ok ? (uint32_t)(px * a.ys + o) * 4u : OOB, 0, SAUX);
         }
     }
 }
