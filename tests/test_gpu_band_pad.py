@@ -91,6 +91,39 @@ def test_gpu_band_kernel_grouped_integer_bitwise(groups):
         np.testing.assert_array_equal(y.float().cpu().numpy(), ref.astype(np.float32))
 
 
+def test_gpu_band_kernel_packed_groups_nonfinite_input():
+    """An infinite input value in group 0. With 32-channel groups each wave's
+    channel step holds one group only, so every output of groups 1-3 equals
+    the oracle's (finite) value. With 16-channel groups, group 1 shares
+    group 0's 32-channel step (its filter zeros meet the infinity: NaN near
+    that pixel, the documented deviation from the per-group sum); groups 2-7
+    are unaffected."""
+    for groups in (4, 8):
+        G = 128 // groups
+        g = torch.Generator().manual_seed(7180 + groups)
+        X = torch.randint(-2, 3, (2, 9, 11, 128), generator=g).to(torch.bfloat16)
+        F = torch.randint(-1, 2, (3, 3, G, 128), generator=g).to(torch.bfloat16)
+        X[1, 4, 5, 3] = float("inf")                     # channel 3: group 0
+        ref = oracle.conv2d_nhwc(X, F, padding=1, groups=groups)
+        out = torch.empty((2, 9, 11, 128), dtype=torch.float32, device=DEV)   # integer sums: exact in fp32
+        y = cf.conv2d_nhwc(X.to(DEV), F.to(DEV), padding=1, groups=groups, out=out).cpu().numpy()
+        torch.cuda.synchronize()
+        clean = slice(G, 128) if groups == 4 else slice(2 * G, 128)
+        np.testing.assert_array_equal(y[..., clean], ref[..., clean].astype(np.float32))
+        assert np.isfinite(ref[..., G:]).all()
+        # group 0: non-finite exactly where the oracle is non-finite, equal elsewhere
+        r0, y0 = ref[..., :G], y[..., :G]
+        np.testing.assert_array_equal(np.isfinite(y0), np.isfinite(r0))
+        np.testing.assert_array_equal(y0[np.isfinite(r0)], r0[np.isfinite(r0)].astype(np.float32))
+        if groups == 8:
+            # the partner group: finite and exact away from the infinite input's window
+            y1 = y[..., G:2 * G]
+            near = np.zeros(y1.shape[:3], dtype=bool)
+            near[1, 3:6, 4:7] = True
+            assert np.isfinite(y1[~near]).all()
+            np.testing.assert_array_equal(y1[~near], ref[..., G:2 * G][~near].astype(np.float32))
+
+
 def test_gpu_band_kernel_repeat_and_coverage():
     """Every output written (Y starts as NaN) and identical bits on a rerun."""
     X = wl.random_tensor((16, 25, 25, 64), 7200).to(torch.bfloat16).to(DEV)
