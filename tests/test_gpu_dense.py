@@ -304,8 +304,16 @@ def test_gpu_calls_allocate_no_device_memory():
     Xd, wd = wl.depthwise_inputs(wl.DW_5X5S2_EXACT)
     Xd, wd = Xd.to(DEV), wd.to(DEV)
     Yd = torch.empty((8, 72, 28, 28), dtype=torch.float32, device=DEV)
+    Xf, Ff = wl.dense_inputs(wl.DENSE_1X1_BF16, dtype="f32")
+    Xf, Ff = Xf.to(DEV), Ff.to(DEV)
+    Yf = torch.empty((32, 28, 28, 512), dtype=torch.float32, device=DEV)
+    Xg = torch.zeros((4, 12, 14, 128), dtype=torch.bfloat16, device=DEV)
+    Fg = torch.zeros((3, 3, 16, 128), dtype=torch.bfloat16, device=DEV)
+    Yg = torch.empty((4, 12, 14, 128), dtype=torch.bfloat16, device=DEV)
     calls = [lambda: cf.conv2d_nhwc(X, F, out=Y),
              lambda: cf.conv2d_nhwc(Xp, Fp, out=Yp),
+             lambda: cf.conv2d_nhwc(Xf, Ff, out=Yf),
+             lambda: cf.conv2d_nhwc(Xg, Fg, out=Yg, padding=1, groups=8),
              lambda: cf.conv2d_nhwc(X[:, 1:, 1:], F, out=Y[:, :55, :55], variant=cf.VARIANT_DIRECT),
              lambda: cf.conv_depthwise(Xd, wd, stride=2, padding=2, exact=True, out=Yd)]
     for c in calls:
